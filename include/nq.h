@@ -1,0 +1,342 @@
+/*
+ * nq.h — C ABI of the MI355X (gfx950) W4A16 paged greedy-decode library (libnq.so).
+ *
+ * What the library computes is the single-token greedy decode step of a
+ * Qwen2-style decoder whose projection weights are symmetric group-wise INT4
+ * (group 128, fp16 scales) and whose activations are fp16, with decode
+ * attention over a paged KV cache of 16 tokens per page, and the capture of
+ * that whole step into one HIP graph. Sources:
+ *   - "How to build your own LLM runtime from scratch" (spokes-wiki), section
+ *     "What it actually builds": INT4 group-128 symmetric weights, paged KV
+ *     cache of 16 tokens per 4 KiB page, fused GEMVs for Q/K/V/O and
+ *     gate/up/down, graph capture of the token loop; greedy sampling only
+ *     (intro paragraph); launch overhead as the dominant cost ("The one lesson
+ *     that generalizes").
+ *   - "How To Build Your Own LLM Runtime From Scratch" (daily.dev), Summary and
+ *     FAQ: fp16 activations with INT4 weights, 28 layers, the block barrier
+ *     that corrupted softmax at partial tail pages.
+ *
+ * Conventions (all entry points):
+ *   - Every call returns nq_status; NQ_OK is 0. nq_last_error() gives a
+ *     thread-local message for the last failing call on this thread.
+ *   - Arguments are validated before anything is enqueued, so a call that
+ *     fails validation has no side effects. No C++ exception crosses the ABI.
+ *   - Device memory is owned by the caller (the library never allocates device
+ *     memory); handles store raw device pointers, which must stay valid while
+ *     the handle (and any graph captured from it) is in use.
+ *   - "stream" is a hipStream_t passed as void*. Nothing in the decode step
+ *     synchronises; results are ready when the stream is.
+ *   - Device pointers that the kernels read with 128-bit loads (packed weights,
+ *     activations, the KV pool, the workspace) must be 16-byte aligned.
+ *   - fp16 means IEEE binary16, passed as raw bits (uint16_t / void*).
+ */
+#ifndef NQ_H
+#define NQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status */
+
+typedef enum nq_status {
+  NQ_OK = 0,
+  NQ_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misalignment, bad enum */
+  NQ_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement     */
+  NQ_ERR_OUT_OF_RANGE = 3,  /* value outside representable / configured range  */
+  NQ_ERR_HIP = 4,           /* a HIP runtime call failed (message has details) */
+  NQ_ERR_STATE = 5,         /* call not allowed in the current state           */
+  NQ_ERR_DEVICE_FAULT = 6   /* a kernel flagged a range error (err_flag != 0)  */
+} nq_status;
+
+/* Name of a status code ("NQ_OK", ...). Never NULL. */
+const char* nq_status_str(nq_status s);
+
+/* Message of the last failing call on the calling thread ("" if none). */
+const char* nq_last_error(void);
+
+/* Version of the packed-weight tile layout described at nq_pack_weights. */
+int32_t nq_layout_version(void);
+
+/* ---------------------------------------------------------- packed weights */
+
+/* Which rows a 16-row tile co-locates, so that a fused epilogue finds the rows
+ * it combines in the same tile. */
+typedef enum nq_mat_kind {
+  NQ_MAT_PLAIN = 0,    /* tile t holds logical rows 16t .. 16t+15                    */
+  NQ_MAT_QKV = 1,      /* fused [Wq; Wk; Wv] (row = head-major, dim-minor). Tile t of
+                          head block hb = t / (d/16), u = t % (d/16): rows r < 8 are
+                          hb*d + 8u + r, rows r >= 8 are hb*d + d/2 + 8u + (r-8), i.e.
+                          the rotate-half RoPE pairs (i, i + d/2) of one head.        */
+  NQ_MAT_GATE_UP = 2,  /* fused [Wg; Wu] with N = 2*I: tile t rows r < 8 are gate rows
+                          8t + r, rows r >= 8 are up rows I + 8t + (r-8).             */
+  NQ_MAT_LM_HEAD = 3   /* same row order as PLAIN                                   */
+} nq_mat_kind;
+
+/* Bytes of the packed form of an N x K matrix: ceil(N/16)*16 * K/2 (codes) +
+ * ceil(N/16)*16 * K/group * 2 (fp16 scales). Returns 0 if the arguments are
+ * invalid (K % group != 0, group != 128, N <= 0). */
+size_t nq_packed_size(int32_t N, int32_t K, int32_t group);
+
+/*
+ * Quantise and repack a float32 weight matrix (host only; no GPU needed).
+ *
+ * Quantisation (symmetric, group-wise along K, group = 128; the pages give the
+ * group size and the symmetric format, section "What it actually builds"):
+ *   a   = max |w[n, 128g .. 128g+127]|                       (float32)
+ *   s16 = fp16_round_half_even(float32(a / 7.0f))
+ *   q   = clamp(round_half_even(double(w) / double(s16)), -8, 7), 0 if s16 == 0
+ * so |w - q*s16| <= s16/2 and the codes used lie in [-7, 7].
+ *
+ * Packed layout, version 1 ("t16g128"): with Np = ceil(N/16)*16, T = Np/16
+ * tiles and G = K/128 groups,
+ *   codes  : T*G blocks of 1024 bytes, block (t, g) at byte (t*G + g)*1024.
+ *            The 16-byte chunk c (0..63) of a block, at byte 16c, holds tile
+ *            row r = c % 16 and K range k0 = 128g + 32*(c/16) .. k0+31, as four
+ *            little-endian 32-bit words; word j holds k0+8j .. k0+8j+7 with
+ *            nibble slot m (bits 4m..4m+3) holding k0 + 8j + (m < 4 ? 2m : 2(m-4)+1),
+ *            stored offset-binary as q + 8.
+ *   scales : at byte T*G*1024: fp16 s16 of (tile t, group g, tile row r) at
+ *            element (t*G + g)*16 + r.
+ *   Tile row r of tile t is the logical row given by nq_mat_kind. Rows beyond
+ *   N (PLAIN / LM_HEAD only) are zero codes (q = 0) with scale 0.
+ *
+ * w         : host float32 [N][K], row-major (torch Linear [out, in] layout).
+ * kind      : row co-location (see nq_mat_kind). QKV needs head_dim % 16 == 0
+ *             and N % head_dim == 0; GATE_UP needs N % 16 == 0.
+ * head_dim  : used by NQ_MAT_QKV only (else ignored).
+ * packed_out: host buffer of nq_packed_size(N, K, group) bytes.
+ * q_out     : optional host int8 [N][K], codes in LOGICAL row order.
+ * s_out     : optional host uint16 [N][K/group], fp16 scale bits, logical order.
+ * Errors: NQ_ERR_INVALID_ARG (null w / packed_out, K % 128, group != 128, bad
+ * kind or shape for kind); NQ_ERR_OUT_OF_RANGE (non-finite weight, or a scale
+ * that overflows fp16). Runs on several host threads.
+ */
+nq_status nq_pack_weights(const float* w, int32_t N, int32_t K, int32_t group,
+                          nq_mat_kind kind, int32_t head_dim, void* packed_out,
+                          int8_t* q_out, uint16_t* s_out);
+
+/* Inverse of the repacking (host): codes and scale bits in logical row order.
+ * Same argument rules as nq_pack_weights; q_out [N][K], s_out [N][K/group]. */
+nq_status nq_unpack_weights(const void* packed, int32_t N, int32_t K, int32_t group,
+                            nq_mat_kind kind, int32_t head_dim, int8_t* q_out,
+                            uint16_t* s_out);
+
+/* Device twin of nq_unpack_weights: decodes every nibble with the same
+ * in-register unpack the GEMV kernels use (fp16 exponent-bias trick) and writes
+ * int8 codes [N][K] and fp16 scale bits [N][K/group] (device pointers) in
+ * logical row order. For bit-exactness tests. */
+nq_status nq_unpack_weights_dev(const void* packed_dev, int32_t N, int32_t K,
+                                int32_t group, nq_mat_kind kind, int32_t head_dim,
+                                int8_t* q_out_dev, uint16_t* s_out_dev, void* stream);
+
+/* ----------------------------------------------------------------- GEMV */
+
+typedef enum nq_epilogue {
+  NQ_EPI_STORE_F16 = 0,    /* y[b][n] = fp16(W x_b)                                   */
+  NQ_EPI_BIAS_F16 = 1,     /* y[b][n] = fp16(W x_b + bias[n])                          */
+  NQ_EPI_RESIDUAL_F16 = 2, /* y[b][n] = fp16(y[b][n] + W x_b)   (y read, then written) */
+  NQ_EPI_SWIGLU_F16 = 3,   /* kind GATE_UP, I = N/2: y[b][j] = fp16(silu(g_j) * u_j),
+                              g_j = (W x_b)[j], u_j = (W x_b)[I + j]; y is [B][I]     */
+  NQ_EPI_STORE_F32 = 4     /* y[b][n] = float32(W x_b)                                 */
+} nq_epilogue;
+
+/*
+ * Batched W4A16 GEMV: y_b = W x_b for b < batch (the fused Q/K/V/O and
+ * gate/up/down projections of "What it actually builds"), fp32 accumulation.
+ *
+ * packed   : device, output of nq_pack_weights for (N, K, kind, head_dim).
+ * batch    : 1 .. 8.
+ * x        : device fp16 [batch][K].
+ * norm_gain: optional device fp16 [K]. If non-NULL the input is first
+ *            RMS-normalised: x_b <- fp16(x_b / sqrt(mean(x_b^2) + eps) * gain).
+ * bias     : device fp16 [N] (logical order), NQ_EPI_BIAS_F16 only.
+ * y        : device output, fp16 or fp32 per the epilogue, [batch][N] (or [batch][N/2]
+ *            for SwiGLU). Must not overlap x (except RESIDUAL, which reads y).
+ * Errors: NQ_ERR_INVALID_ARG for null/misaligned pointers, K % 128, batch out
+ * of 1..8, or an epilogue that does not fit the kind. NQ_ERR_HIP on launch.
+ */
+nq_status nq_gemv_w4a16(const void* packed, int32_t N, int32_t K, nq_mat_kind kind,
+                        int32_t head_dim, int32_t batch, const void* x,
+                        const void* norm_gain, float eps, const void* bias, void* y,
+                        nq_epilogue epi, void* stream);
+
+/* ------------------------------------------------------------ model config */
+
+typedef struct nq_config {
+  int32_t layers;        /* decoder layers (28 for the 7B shape)                        */
+  int32_t hidden;        /* H, multiple of 128                                          */
+  int32_t intermediate;  /* I, multiple of 128                                          */
+  int32_t n_heads;       /* query heads                                                 */
+  int32_t n_kv_heads;    /* KV heads; n_heads % n_kv_heads == 0, ratio <= 8             */
+  int32_t head_dim;      /* d: 64 or 128                                                */
+  int32_t vocab;         /* V                                                           */
+  float rms_eps;         /* RMSNorm epsilon (1e-6)                                      */
+  float rope_theta;      /* RoPE base (1e6)                                             */
+  int32_t group;         /* quantisation group, must be 128                             */
+  int32_t page_tokens;   /* tokens per KV page, must be 16                              */
+  int32_t max_batch;     /* largest batch a step will be called with (1 .. 8)           */
+  int32_t max_pos;       /* positions covered by the RoPE table (max context length)    */
+} nq_config;
+
+/* Checks a configuration; NQ_OK or NQ_ERR_INVALID_ARG / NQ_ERR_UNSUPPORTED. */
+nq_status nq_config_check(const nq_config* cfg);
+
+/* ---------------------------------------------------------------- KV cache */
+
+/*
+ * Paged KV cache ("What it actually builds": 16 tokens per 4 KiB page, pages
+ * reached through a page table). The pool is caller-owned device memory:
+ *   pool[layer][0 = K, 1 = V][page][kv_head][slot 0..15][head_dim]  fp16
+ * so one (layer, K or V, page, kv_head) block is 16 * head_dim fp16 (4096 bytes
+ * at head_dim 128). Token p of sequence b is in page page_table[b][p / 16],
+ * slot p % 16. Page ids are chosen by the caller (any permutation of the pool;
+ * -1 marks an unused table entry). K is stored after RoPE.
+ */
+typedef struct nq_kv nq_kv;
+
+size_t nq_kv_pool_bytes(const nq_config* cfg, int32_t num_pages);
+
+/* Builds a descriptor over a caller-owned pool of num_pages pages (bytes must be
+ * at least nq_kv_pool_bytes). No device work. */
+nq_status nq_kv_alloc(const nq_config* cfg, void* pool_dev, size_t bytes,
+                      int32_t num_pages, nq_kv** out);
+
+/*
+ * Writes one token's K and V per sequence into the pool:
+ *   pool[layer][0][pt[b][pos[b]/16]][h][pos[b]%16][:] = k[b][h][:]  (and V likewise)
+ * page_table: device int32 [batch][max_pages]; pos: device int32 [batch];
+ * k, v: device fp16 [batch][n_kv_heads][head_dim].
+ * err_flag: optional device int32; a position beyond max_pages*16, or a page id
+ * outside [0, num_pages), skips that write and ORs 1 into *err_flag
+ * (see nq_check_device_error).
+ */
+nq_status nq_kv_append(nq_kv* kv, int32_t layer, int32_t batch, const int32_t* page_table,
+                       int32_t max_pages, const int32_t* pos, const void* k, const void* v,
+                       int32_t* err_flag, void* stream);
+
+void nq_kv_free(nq_kv* kv);
+
+/* ----------------------------------------------------- decode attention */
+
+/* Scratch bytes nq_attn_decode needs for its split-K partials. */
+size_t nq_attn_workspace_bytes(const nq_config* cfg, int32_t batch, int32_t max_pages);
+
+/*
+ * Split-K paged decode attention for one layer (GQA): for query head h of
+ * sequence b, with kv = h / (n_heads / n_kv_heads),
+ *   o[b][h] = sum_t softmax_t(q[b][h] . k_t / sqrt(d)) v_t   over t < lens[b]
+ * (scaled dot-product attention with a stable softmax; "Build Crude
+ * Implementations for Learning", "nanoGPT level", and the "Inference Zero To
+ * Hero" preface). Partial tail pages are handled: slots at or beyond lens[b]
+ * are never used, whatever they hold.
+ * q: device fp16 [batch][n_heads][head_dim]; out: device fp16, same shape.
+ * lens: device int32 [batch] (0 gives a zero output row).
+ * workspace: device, nq_attn_workspace_bytes(cfg, batch, max_pages) bytes.
+ * err_flag: optional device int32 (bad page id or length -> ORs 2, output 0).
+ */
+nq_status nq_attn_decode(const nq_kv* kv, int32_t layer, int32_t batch, const void* q,
+                         const int32_t* page_table, int32_t max_pages, const int32_t* lens,
+                         void* out, void* workspace, size_t ws_bytes, int32_t* err_flag,
+                         void* stream);
+
+/* -------------------------------------------------------------- the model */
+
+typedef struct nq_model nq_model;
+
+/* Per-layer device pointers (all caller-owned). */
+typedef struct nq_layer_ptrs {
+  const void* qkv_packed;      /* nq_pack_weights(kind QKV) of [Wq; Wk; Wv], N = (nh+2nkv)d, K = H */
+  const void* qkv_bias;        /* fp16 [(nh + 2 nkv) d], logical order                             */
+  const void* o_packed;        /* PLAIN, N = H, K = nh d                                           */
+  const void* gate_up_packed;  /* GATE_UP of [Wg; Wu], N = 2I, K = H                               */
+  const void* down_packed;     /* PLAIN, N = H, K = I                                              */
+  const void* attn_norm;       /* fp16 [H] RMSNorm gain before attention                           */
+  const void* mlp_norm;        /* fp16 [H] RMSNorm gain before the MLP                             */
+} nq_layer_ptrs;
+
+nq_status nq_model_create(const nq_config* cfg, nq_model** out);
+nq_status nq_model_bind_layer(nq_model* m, int32_t layer, const nq_layer_ptrs* p);
+/* embed: fp16 [V][H]; final_norm: fp16 [H]; lm_packed: kind LM_HEAD, N = V, K = H. */
+nq_status nq_model_bind_head(nq_model* m, const void* embed, const void* final_norm,
+                             const void* lm_packed);
+
+/* RoPE table: float32 [max_pos][head_dim/2][2] = (cos, sin) of
+ * pos * theta^(-2i/d), computed on the host in double precision. */
+size_t nq_rope_table_bytes(const nq_config* cfg);
+nq_status nq_rope_table_fill(const nq_config* cfg, float* host_out);
+nq_status nq_model_bind_rope(nq_model* m, const void* rope_table_dev);
+
+/* Scratch the decode step needs at a given batch and page-table width. The
+ * workspace must be zero-filled by the caller once, before its first use; the
+ * library leaves its counters at zero between steps. */
+size_t nq_workspace_bytes(const nq_config* cfg, int32_t batch, int32_t max_pages);
+nq_status nq_model_bind_workspace(nq_model* m, void* ws_dev, size_t bytes);
+
+void nq_model_destroy(nq_model* m);
+
+/* ------------------------------------------------------------ decode step */
+
+typedef struct nq_step_io {
+  int32_t batch;            /* 1 .. cfg.max_batch                                          */
+  int32_t max_pages;        /* page_table row stride (pages per sequence)                  */
+  const int32_t* page_table;/* device int32 [batch][max_pages]                             */
+  int32_t* tokens;          /* device int32 [batch]: in = token at pos, out = greedy next  */
+  int32_t* pos;             /* device int32 [batch]: in = position of the input token;
+                               the step appends K/V there and adds 1                       */
+  float* logits;            /* optional device float32 [batch][vocab]                      */
+  void* layer_out;          /* optional device fp16 [layers][batch][H]: hidden state after
+                               each layer (debug; may be captured)                         */
+  int32_t* token_hist;      /* optional device int32 [batch][hist_len]: the step writes
+                               token_hist[b][pos+1] = next token (if pos+1 < hist_len)     */
+  int32_t hist_len;
+  int32_t* err_flag;        /* optional device int32: device-side range errors OR bits in
+                               (1 = KV write, 2 = attention read, 4 = token id, 8 = NaN
+                               logits); NULL uses a flag inside the workspace              */
+} nq_step_io;
+
+/*
+ * One greedy decode step for a batch (everything on the device, enqueued on
+ * stream): embedding gather; per layer RMSNorm -> fused QKV GEMV + bias ->
+ * RoPE -> K/V page append at pos -> split-K paged attention over [0, pos] ->
+ * O GEMV + residual -> RMSNorm -> gate/up GEMV + SwiGLU -> down GEMV +
+ * residual; final RMSNorm -> LM-head GEMV -> argmax (lowest index on ties)
+ * -> tokens, pos += 1.
+ * Errors: NQ_ERR_STATE if the model is not fully bound; NQ_ERR_INVALID_ARG for
+ * bad io; NQ_ERR_HIP on launch failure.
+ */
+nq_status nq_decode_step(nq_model* m, nq_kv* kv, const nq_step_io* io, void* stream);
+
+/* ---------------------------------------------------------- graph capture */
+
+/*
+ * Captures one decode step (the same kernels as nq_decode_step) into a HIP
+ * graph, so that a token costs one launch ("What it actually builds": graph
+ * capture of the token-generation loop; "The one lesson that generalizes").
+ * Every per-step value lives in device memory (tokens, pos, page table), so
+ * replays chain with no host updates. batch and max_pages are fixed per graph.
+ * Errors: NQ_ERR_STATE for the null stream or a stream already capturing.
+ */
+typedef struct nq_graph nq_graph;
+
+nq_status nq_graph_capture(nq_model* m, nq_kv* kv, const nq_step_io* io, void* stream,
+                           nq_graph** out);
+nq_status nq_graph_launch(nq_graph* g, void* stream);
+/* Number of kernel nodes in the captured step. */
+int32_t nq_graph_kernel_count(const nq_graph* g);
+void nq_graph_destroy(nq_graph* g);
+
+/* ---------------------------------------------------------------- errors */
+
+/* Synchronises stream, reads *err_flag_dev, and returns NQ_ERR_DEVICE_FAULT (with
+ * the flag bits in the message) if it is non-zero; the flag is then reset to 0. */
+nq_status nq_check_device_error(int32_t* err_flag_dev, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NQ_H */

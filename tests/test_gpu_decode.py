@@ -1,0 +1,175 @@
+"""End-to-end GPU decode parity against the oracle (tiny Qwen2-style config).
+
+Run: 16-token prompt, 32 greedy tokens, KV in 16-token pages ending on a
+partial page (47 cached positions = 2 full pages + 15)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle.model import OracleModel, layer_causal, head_logits
+from w4a16_gemv_paged_amd.engine import DeviceModel, KVCache, Stepper, run_greedy
+from gpu_util import F16, rel_inf, say
+
+pytestmark = pytest.mark.gpu
+
+SHAPE = synth.TINY
+PROMPT_LEN, N_GEN = 16, 32
+TOL_LAYER, TOL_LOGITS, MARGIN = 2e-3, 5e-3, 1e-2
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    layers = [synth.layer_params(SHAPE, i, seed=0) for i in range(SHAPE.layers)]
+    head = synth.head_params(SHAPE, seed=0)
+    om = OracleModel.build(SHAPE, layers, head)
+    say("build tiny device model")
+    dm = DeviceModel(SHAPE, lambda i: layers[i], head, max_batch=8, max_pos=4096)
+    yield om, dm
+    dm.close()
+
+
+def _run(dm, prompts, n_gen, graph=False, pages=None, seed=3, layers=True):
+    B = len(prompts)
+    need = max(len(p) for p in prompts) + n_gen
+    max_pages = pages or (need + 15) // 16
+    pt, total = synth.decode_page_tables(B, max_pages, seed=seed, spare_pages=3)
+    kv = KVCache(dm, total, poison=True)
+    st = Stepper(dm, kv, pt, hist_len=need + 1, want_logits=True, want_layers=layers)
+    stream = torch.cuda.Stream() if graph else torch.cuda.current_stream()   # capture needs a non-null stream
+    with torch.cuda.stream(stream):
+        out = run_greedy(st, prompts, n_gen, use_graph=graph, stream=stream, record_logits=True,
+                         record_layers=layers)
+    torch.cuda.synchronize()
+    out["pool"] = kv.pool.cpu().numpy()
+    out["page_table"] = pt
+    out["hist"] = st.hist.cpu().numpy()
+    out["kernels"] = None
+    if graph:
+        from w4a16_gemv_paged_amd import nq_graph_kernel_count
+        out["kernels"] = nq_graph_kernel_count(st.graph)
+    st.close()
+    kv.close()
+    return out
+
+
+@pytest.fixture(scope="module")
+def tiny_run(tiny):
+    om, dm = tiny
+    prompt = synth.prompt_ids(PROMPT_LEN, SHAPE.vocab, seed=2)
+    say("tiny eager run")
+    gpu = _run(dm, [prompt], N_GEN)
+    orc = oracle.generate(om, prompt, N_GEN, forced=gpu["tokens"][0])
+    return prompt, gpu, orc
+
+
+def test_tokens_match_where_margin_is_clear(tiny_run):
+    prompt, gpu, orc = tiny_run
+    ok = orc["margins"] > MARGIN
+    assert ok.sum() >= N_GEN // 2          # the gate must not be vacuous
+    np.testing.assert_array_equal(gpu["tokens"][0][ok], orc["tokens"][ok])
+
+
+def test_logits_within_tolerance(tiny_run):
+    prompt, gpu, orc = tiny_run
+    gl = gpu["logits"][PROMPT_LEN - 1:, 0]
+    assert gl.shape == orc["logits"].shape
+    errs = [rel_inf(gl[i], orc["logits"][i]) for i in range(N_GEN)]
+    assert max(errs) < TOL_LOGITS, max(errs)
+
+
+def test_each_layer_teacher_forced(tiny_run, tiny):
+    """Layer l recomputed by the oracle from the GPU's own layer l-1 output at
+    every position (the oracle's own KV for those inputs)."""
+    om, dm = tiny
+    prompt, gpu, orc = tiny_run
+    fed = list(prompt) + list(gpu["tokens"][0][:-1])
+    lo = gpu["layer_out"][:, :, 0]                     # [T, L, H]
+    x = om.head.embed[np.array(fed)]
+    for li in range(SHAPE.layers):
+        ref = layer_causal(om.layers[li], om.dims, x)
+        errs = [rel_inf(lo[t, li], ref[t]) for t in range(len(fed))]
+        assert max(errs) < TOL_LAYER, (li, max(errs))
+        x = lo[:, li]
+    z = head_logits(om, lo[:, -1])
+    errs = [rel_inf(gpu["logits"][t, 0], z[t]) for t in range(PROMPT_LEN - 1, len(fed))]
+    assert max(errs) < TOL_LOGITS
+
+
+def test_free_running_layers_within_tolerance(tiny_run):
+    prompt, gpu, orc = tiny_run
+    lo = gpu["layer_out"][:, :, 0]
+    olo = orc["layer_out"]                              # [T, L, H]
+    errs = [rel_inf(lo[t, li], olo[t, li]) for t in range(lo.shape[0]) for li in range(SHAPE.layers)]
+    assert max(errs) < 5e-3, max(errs)
+
+
+def test_kv_pool_contents_and_untouched_slots(tiny_run, tiny):
+    """K (after RoPE) and V in the pool match the oracle's projections of the
+    GPU's layer inputs; slots past the last position keep their NaN poison."""
+    om, dm = tiny
+    prompt, gpu, orc = tiny_run
+    fed = list(prompt) + list(gpu["tokens"][0][:-1])
+    T = len(fed)
+    cfg = dm.cfg
+    pool = gpu["pool"].view(F16).reshape(cfg.layers, 2, -1, cfg.n_kv_heads, 16, cfg.head_dim)
+    kvm = oracle.PagedKVEmu(cfg.layers, pool.shape[2], cfg.n_kv_heads, cfg.head_dim, gpu["page_table"], pool=pool)
+    lo = gpu["layer_out"][:, :, 0]
+    x = om.head.embed[np.array(fed)]
+    d, nh, nkv = cfg.head_dim, cfg.n_heads, cfg.n_kv_heads
+    for li in range(cfg.layers):
+        L = om.layers[li]
+        xn = oracle.rmsnorm(x, L.g1, 1e-6)
+        qkv = (xn.astype(np.float64) @ L.w("qkv").T + L.b_qkv.astype(np.float64)).astype(F16)
+        k = oracle.rope(qkv[:, nh * d:(nh + nkv) * d].reshape(T, nkv, d), np.arange(T), 1e6)
+        v = qkv[:, (nh + nkv) * d:].reshape(T, nkv, d)
+        kg, vg = kvm.get(li, 0, T)
+        assert rel_inf(kg, k) < TOL_LAYER and rel_inf(vg, v) < TOL_LAYER
+        x = lo[:, li]
+    last_page = gpu["page_table"][0, (T - 1) // 16]
+    tail = pool[:, :, last_page, :, (T - 1) % 16 + 1:]
+    assert np.all(np.isnan(tail.astype(np.float32)))
+
+
+def test_token_history_written(tiny_run):
+    prompt, gpu, orc = tiny_run
+    hist = gpu["hist"][0]
+    np.testing.assert_array_equal(hist[PROMPT_LEN:PROMPT_LEN + N_GEN], gpu["tokens"][0])
+
+
+def test_graph_replay_equals_eager_bitwise(tiny, tiny_run):
+    om, dm = tiny
+    prompt, eager, _ = tiny_run
+    say("tiny graph run")
+    g = _run(dm, [prompt], N_GEN, graph=True)
+    np.testing.assert_array_equal(g["tokens"], eager["tokens"])
+    np.testing.assert_array_equal(g["logits"].view(np.uint32), eager["logits"].view(np.uint32))
+    np.testing.assert_array_equal(g["layer_out"].view(np.uint16), eager["layer_out"].view(np.uint16))
+    assert g["kernels"] == 1 + 6 * SHAPE.layers + 2
+
+
+def test_batched_ragged_equals_single_sequences(tiny):
+    """B = 4 with ragged prompts gives, per sequence, what B = 1 gives."""
+    om, dm = tiny
+    prompts = [synth.prompt_ids(n, SHAPE.vocab, seed=20 + n) for n in (5, 16, 9, 23)]
+    say("tiny batched run")
+    bat = _run(dm, prompts, 8, layers=False)
+    for b, p in enumerate(prompts):
+        say("tiny single run", b)
+        one = _run(dm, [p], 8, layers=False)
+        np.testing.assert_array_equal(bat["tokens"][b], one["tokens"][0])
+
+
+def test_batch8_logits_against_oracle(tiny):
+    om, dm = tiny
+    prompts = [synth.prompt_ids(n, SHAPE.vocab, seed=40 + n) for n in (3, 7, 12, 16, 4, 9, 2, 14)]
+    say("tiny batch-8 run")
+    gpu = _run(dm, prompts, 4, layers=False)
+    for b, p in enumerate(prompts):
+        orc = oracle.generate(om, p, 4, forced=gpu["tokens"][b])
+        steps = range(len(p) - 1, len(p) + 3)
+        for i, s in enumerate(steps):
+            assert rel_inf(gpu["logits"][s, b], orc["logits"][i]) < TOL_LOGITS
+        ok = orc["margins"] > MARGIN
+        np.testing.assert_array_equal(gpu["tokens"][b][ok], orc["tokens"][ok])

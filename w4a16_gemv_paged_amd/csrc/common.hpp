@@ -1,0 +1,116 @@
+// Internal declarations shared by the host code and the kernel launchers of libnq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstddef>
+#include <cstdint>
+
+#include "nq.h"
+
+namespace nq {
+
+constexpr int kTileRows = 16;      // rows per packed tile
+constexpr int kGroup = 128;        // quantisation group along K
+constexpr int kBlockBytes = 1024;  // packed codes of one (tile, group)
+constexpr int kPageTokens = 16;    // KV tokens per page
+constexpr int kMaxBatch = 8;
+
+// Record a message for nq_last_error() and return s.
+nq_status fail(nq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+nq_status hip_fail(hipError_t e, const char* what);
+void clear_error();
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Logical row held by tile row r of tile t (see nq_mat_kind).
+__host__ __device__ inline int64_t tile_row_logical(int kind, int64_t N, int head_dim, int64_t t,
+                                                    int r) {
+  if (kind == NQ_MAT_QKV) {
+    const int64_t tiles_per_head = head_dim / 16;
+    const int64_t hb = t / tiles_per_head, u = t % tiles_per_head;
+    return hb * head_dim + (r < 8 ? 8 * u + r : head_dim / 2 + 8 * u + (r - 8));
+  }
+  if (kind == NQ_MAT_GATE_UP) {
+    const int64_t half = N / 2;
+    return r < 8 ? 8 * t + r : half + 8 * t + (r - 8);
+  }
+  return 16 * t + r;
+}
+
+// Validates (N, K, group, kind, head_dim) for packing; sets the error message.
+nq_status check_pack_args(int32_t N, int32_t K, int32_t group, nq_mat_kind kind, int32_t head_dim);
+
+inline int64_t padded_rows(int32_t N) { return (static_cast<int64_t>(N) + 15) / 16 * 16; }
+inline int64_t tiles_of(int32_t N) { return padded_rows(N) / 16; }
+inline size_t codes_bytes(int32_t N, int32_t K) {
+  return static_cast<size_t>(tiles_of(N)) * (K / kGroup) * kBlockBytes;
+}
+
+// ------------------------------------------------------------------ kernels
+
+// Internal epilogues beyond the public nq_epilogue values.
+enum InternalEpi : int {
+  EPI_QKV_ROPE_KV = 16,  // bias, RoPE on q/k, q -> qbuf, k/v -> KV pool (decode step)
+};
+
+struct GemvArgs {
+  const void* packed = nullptr;
+  int32_t N = 0, K = 0, kind = 0, head_dim = 0, batch = 1;
+  const void* x = nullptr;          // fp16 [B][K]
+  const void* norm_gain = nullptr;  // fp16 [K] or null
+  float eps = 1e-6f;
+  const void* bias = nullptr;       // fp16 [N]
+  void* y = nullptr;                // output
+  void* y2 = nullptr;               // optional copy of the residual output (layer_out)
+  int epi = 0;
+  // argmax partials (LM head in the step): float [B][T] values, int [B][T] indices
+  float* amax_val = nullptr;
+  int32_t* amax_idx = nullptr;
+  // QKV epilogue
+  const int32_t* pos = nullptr;
+  const int32_t* page_table = nullptr;
+  int32_t max_pages = 0, num_pages = 0, n_heads = 0, n_kv = 0;
+  void* kv_k = nullptr;             // layer's K pool base
+  void* kv_v = nullptr;             // layer's V pool base
+  const float* rope = nullptr;      // [max_pos][d/2][2]
+  int32_t max_pos = 0;
+  int32_t* err = nullptr;
+};
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const void* q = nullptr;          // fp16 [B][nh][d]
+  const void* k_pool = nullptr;     // layer K base: [page][nkv][16][d]
+  const void* v_pool = nullptr;
+  const int32_t* page_table = nullptr;
+  int32_t max_pages = 0, num_pages = 0;
+  const int32_t* lens = nullptr;    // [B]
+  int32_t len_add = 0;              // 1 when lens points at positions (decode step)
+  void* out = nullptr;              // fp16 [B][nh][d]
+  float* part_o = nullptr;          // [B][nh][S][d]
+  float* part_ml = nullptr;         // [B][nh][S][2]
+  int32_t batch = 1, n_heads = 0, n_kv = 0, head_dim = 0, splits = 1;
+  int32_t* err = nullptr;
+};
+int attn_splits_for(int32_t max_pages);
+size_t attn_partial_bytes(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t splits);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+hipError_t launch_kv_append(void* k_pool, void* v_pool, int32_t batch, int32_t n_kv,
+                            int32_t head_dim, const int32_t* page_table, int32_t max_pages,
+                            int32_t num_pages, const int32_t* pos, const void* k, const void* v,
+                            int32_t* err, hipStream_t s);
+
+hipError_t launch_embed(const void* embed, int32_t vocab, int32_t hidden, const int32_t* tokens,
+                        int32_t batch, void* h, int32_t* err, hipStream_t s);
+
+hipError_t launch_argmax_finalize(const float* vals, const int32_t* idx, int32_t tiles,
+                                  int32_t batch, int32_t vocab, int32_t* tokens, int32_t* pos,
+                                  int32_t* hist, int32_t hist_len, int32_t* err, hipStream_t s);
+
+hipError_t launch_unpack_dev(const void* packed, int32_t N, int32_t K, int32_t kind,
+                             int32_t head_dim, int8_t* q_out, uint16_t* s_out, hipStream_t s);
+
+}  // namespace nq

@@ -1,0 +1,509 @@
+// Host runtime of libnq: model and KV-cache handles, the decode-step driver,
+// HIP-graph capture of the step, and the kernel-level entry points.
+//
+// The step enqueues, per layer, the fused projections of "How to build your own
+// LLM runtime from scratch" ("What it actually builds") and the paged decode
+// attention, then the LM head and the greedy argmax; capturing that sequence in
+// one graph turns a token into one launch ("The one lesson that generalizes").
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "common.hpp"
+
+using namespace nq;
+
+struct nq_model {
+  nq_config cfg{};
+  std::vector<nq_layer_ptrs> layers;
+  std::vector<char> bound;
+  const void* embed = nullptr;
+  const void* final_norm = nullptr;
+  const void* lm = nullptr;
+  const float* rope = nullptr;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+};
+
+struct nq_kv {
+  nq_config cfg{};
+  void* pool = nullptr;
+  size_t bytes = 0;
+  int32_t num_pages = 0;
+};
+
+struct nq_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int32_t kernels = 0;
+};
+
+namespace {
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct Workspace {
+  int32_t* err;
+  void* h;
+  void* qbuf;
+  void* attn_o;
+  void* act;
+  float* part_o;
+  float* part_ml;
+  float* amax_val;
+  int32_t* amax_idx;
+  int splits;
+  size_t total;
+};
+
+Workspace carve(const nq_config& c, int32_t batch, int32_t max_pages, uint8_t* base) {
+  Workspace w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    uint8_t* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  const int32_t qd = c.n_heads * c.head_dim;
+  w.splits = attn_splits_for(max_pages);
+  w.err = reinterpret_cast<int32_t*>(take(256));
+  w.h = take(static_cast<size_t>(batch) * c.hidden * 2);
+  w.qbuf = take(static_cast<size_t>(batch) * qd * 2);
+  w.attn_o = take(static_cast<size_t>(batch) * qd * 2);
+  w.act = take(static_cast<size_t>(batch) * c.intermediate * 2);
+  w.part_o = reinterpret_cast<float*>(take(static_cast<size_t>(batch) * c.n_heads * w.splits * c.head_dim * 4));
+  w.part_ml = reinterpret_cast<float*>(take(static_cast<size_t>(batch) * c.n_heads * w.splits * 2 * 4));
+  const int64_t T = tiles_of(c.vocab);
+  w.amax_val = reinterpret_cast<float*>(take(static_cast<size_t>(batch) * T * 4));
+  w.amax_idx = reinterpret_cast<int32_t*>(take(static_cast<size_t>(batch) * T * 4));
+  w.total = off;
+  return w;
+}
+
+size_t layer_pool_elems(const nq_config& c, int32_t num_pages) {
+  return static_cast<size_t>(num_pages) * c.n_kv_heads * kPageTokens * c.head_dim;
+}
+
+nq_status check_io(const nq_model* m, const nq_step_io* io) {
+  if (!io) return fail(NQ_ERR_INVALID_ARG, "null step io");
+  if (io->batch < 1 || io->batch > m->cfg.max_batch)
+    return fail(NQ_ERR_INVALID_ARG, "batch %d outside 1..%d", io->batch, m->cfg.max_batch);
+  if (io->max_pages < 1) return fail(NQ_ERR_INVALID_ARG, "max_pages must be >= 1");
+  if (!io->page_table || !io->tokens || !io->pos)
+    return fail(NQ_ERR_INVALID_ARG, "page_table, tokens and pos are required");
+  if (io->token_hist && io->hist_len < 1) return fail(NQ_ERR_INVALID_ARG, "hist_len must be >= 1");
+  return NQ_OK;
+}
+
+nq_status check_model_ready(const nq_model* m, const nq_kv* kv, const nq_step_io* io) {
+  if (!m || !kv) return fail(NQ_ERR_INVALID_ARG, "null model or kv");
+  for (int i = 0; i < m->cfg.layers; ++i)
+    if (!m->bound[i]) return fail(NQ_ERR_STATE, "layer %d not bound", i);
+  if (!m->embed || !m->final_norm || !m->lm) return fail(NQ_ERR_STATE, "head not bound");
+  if (!m->rope) return fail(NQ_ERR_STATE, "RoPE table not bound");
+  if (!m->ws) return fail(NQ_ERR_STATE, "workspace not bound");
+  nq_status st = check_io(m, io);
+  if (st != NQ_OK) return st;
+  const Workspace w = carve(m->cfg, io->batch, io->max_pages, nullptr);
+  if (w.total > m->ws_bytes)
+    return fail(NQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", m->ws_bytes, w.total);
+  const nq_config& a = m->cfg;
+  const nq_config& b = kv->cfg;
+  if (a.layers != b.layers || a.n_kv_heads != b.n_kv_heads || a.head_dim != b.head_dim)
+    return fail(NQ_ERR_INVALID_ARG, "KV cache config does not match the model");
+  return NQ_OK;
+}
+
+// Enqueue one decode step. Returns the number of kernels launched (>= 0) or -1.
+int enqueue_step(nq_model* m, nq_kv* kv, const nq_step_io* io, hipStream_t s) {
+  const nq_config& c = m->cfg;
+  const int B = io->batch;
+  Workspace w = carve(c, B, io->max_pages, static_cast<uint8_t*>(m->ws));
+  int32_t* err = io->err_flag ? io->err_flag : w.err;
+  const int qkv_n = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const size_t lp = layer_pool_elems(c, kv->num_pages);
+  uint16_t* pool = static_cast<uint16_t*>(kv->pool);
+  int launches = 0;
+  hipError_t e = launch_embed(m->embed, c.vocab, c.hidden, io->tokens, B, w.h, err, s);
+  if (e != hipSuccess) return hip_fail(e, "embed launch"), -1;
+  ++launches;
+  for (int l = 0; l < c.layers; ++l) {
+    const nq_layer_ptrs& L = m->layers[l];
+    uint16_t* kbase = pool + static_cast<size_t>(l) * 2 * lp;
+    uint16_t* vbase = kbase + lp;
+
+    GemvArgs q{};
+    q.packed = L.qkv_packed;
+    q.N = qkv_n;
+    q.K = c.hidden;
+    q.kind = NQ_MAT_QKV;
+    q.head_dim = c.head_dim;
+    q.batch = B;
+    q.x = w.h;
+    q.norm_gain = L.attn_norm;
+    q.eps = c.rms_eps;
+    q.bias = L.qkv_bias;
+    q.y = w.qbuf;
+    q.epi = EPI_QKV_ROPE_KV;
+    q.pos = io->pos;
+    q.page_table = io->page_table;
+    q.max_pages = io->max_pages;
+    q.num_pages = kv->num_pages;
+    q.n_heads = c.n_heads;
+    q.n_kv = c.n_kv_heads;
+    q.kv_k = kbase;
+    q.kv_v = vbase;
+    q.rope = m->rope;
+    q.max_pos = c.max_pos;
+    q.err = err;
+    if ((e = launch_gemv(q, s)) != hipSuccess) return hip_fail(e, "qkv gemv launch"), -1;
+
+    AttnArgs at{};
+    at.q = w.qbuf;
+    at.k_pool = kbase;
+    at.v_pool = vbase;
+    at.page_table = io->page_table;
+    at.max_pages = io->max_pages;
+    at.num_pages = kv->num_pages;
+    at.lens = io->pos;
+    at.len_add = 1;
+    at.out = w.attn_o;
+    at.part_o = w.part_o;
+    at.part_ml = w.part_ml;
+    at.batch = B;
+    at.n_heads = c.n_heads;
+    at.n_kv = c.n_kv_heads;
+    at.head_dim = c.head_dim;
+    at.splits = w.splits;
+    at.err = err;
+    if ((e = launch_attention(at, s)) != hipSuccess) return hip_fail(e, "attention launch"), -1;
+
+    GemvArgs o{};
+    o.packed = L.o_packed;
+    o.N = c.hidden;
+    o.K = c.n_heads * c.head_dim;
+    o.kind = NQ_MAT_PLAIN;
+    o.batch = B;
+    o.x = w.attn_o;
+    o.y = w.h;
+    o.epi = NQ_EPI_RESIDUAL_F16;
+    o.err = err;
+    if ((e = launch_gemv(o, s)) != hipSuccess) return hip_fail(e, "o gemv launch"), -1;
+
+    GemvArgs gu{};
+    gu.packed = L.gate_up_packed;
+    gu.N = 2 * c.intermediate;
+    gu.K = c.hidden;
+    gu.kind = NQ_MAT_GATE_UP;
+    gu.batch = B;
+    gu.x = w.h;
+    gu.norm_gain = L.mlp_norm;
+    gu.eps = c.rms_eps;
+    gu.y = w.act;
+    gu.epi = NQ_EPI_SWIGLU_F16;
+    gu.err = err;
+    if ((e = launch_gemv(gu, s)) != hipSuccess) return hip_fail(e, "gate/up gemv launch"), -1;
+
+    GemvArgs dn{};
+    dn.packed = L.down_packed;
+    dn.N = c.hidden;
+    dn.K = c.intermediate;
+    dn.kind = NQ_MAT_PLAIN;
+    dn.batch = B;
+    dn.x = w.act;
+    dn.y = w.h;
+    dn.y2 = io->layer_out ? static_cast<uint16_t*>(io->layer_out) + static_cast<size_t>(l) * B * c.hidden : nullptr;
+    dn.epi = NQ_EPI_RESIDUAL_F16;
+    dn.err = err;
+    if ((e = launch_gemv(dn, s)) != hipSuccess) return hip_fail(e, "down gemv launch"), -1;
+    launches += 6;
+  }
+  GemvArgs lm{};
+  lm.packed = m->lm;
+  lm.N = c.vocab;
+  lm.K = c.hidden;
+  lm.kind = NQ_MAT_LM_HEAD;
+  lm.batch = B;
+  lm.x = w.h;
+  lm.norm_gain = m->final_norm;
+  lm.eps = c.rms_eps;
+  lm.y = io->logits;
+  lm.epi = NQ_EPI_STORE_F32;
+  lm.amax_val = w.amax_val;
+  lm.amax_idx = w.amax_idx;
+  lm.err = err;
+  if ((e = launch_gemv(lm, s)) != hipSuccess) return hip_fail(e, "lm head launch"), -1;
+  e = launch_argmax_finalize(w.amax_val, w.amax_idx, static_cast<int32_t>(tiles_of(c.vocab)), B, c.vocab,
+                             io->tokens, io->pos, io->token_hist, io->hist_len, err, s);
+  if (e != hipSuccess) return hip_fail(e, "argmax launch"), -1;
+  return launches + 2;
+}
+
+}  // namespace
+
+extern "C" {
+
+nq_status nq_gemv_w4a16(const void* packed, int32_t N, int32_t K, nq_mat_kind kind, int32_t head_dim,
+                        int32_t batch, const void* x, const void* norm_gain, float eps, const void* bias,
+                        void* y, nq_epilogue epi, void* stream) {
+  nq_status st = check_pack_args(N, K, kGroup, kind, head_dim);
+  if (st != NQ_OK) return st;
+  if (!packed || !x || !y) return fail(NQ_ERR_INVALID_ARG, "nq_gemv_w4a16: null packed, x or y");
+  if (!aligned16(packed) || !aligned16(x) || (norm_gain && !aligned16(norm_gain)))
+    return fail(NQ_ERR_INVALID_ARG, "nq_gemv_w4a16: packed, x and norm_gain must be 16-byte aligned");
+  if (batch < 1 || batch > kMaxBatch) return fail(NQ_ERR_INVALID_ARG, "batch %d outside 1..8", batch);
+  if (epi < NQ_EPI_STORE_F16 || epi > NQ_EPI_STORE_F32)
+    return fail(NQ_ERR_INVALID_ARG, "unknown epilogue %d", static_cast<int>(epi));
+  if (epi == NQ_EPI_SWIGLU_F16 && kind != NQ_MAT_GATE_UP)
+    return fail(NQ_ERR_INVALID_ARG, "SwiGLU epilogue needs a GATE_UP matrix");
+  if (epi != NQ_EPI_SWIGLU_F16 && kind == NQ_MAT_GATE_UP)
+    return fail(NQ_ERR_INVALID_ARG, "a GATE_UP matrix needs the SwiGLU epilogue");
+  if (epi == NQ_EPI_BIAS_F16 && !bias) return fail(NQ_ERR_INVALID_ARG, "bias epilogue needs bias");
+  if (!(eps > 0.0f) && norm_gain) return fail(NQ_ERR_INVALID_ARG, "eps must be > 0");
+  GemvArgs a{};
+  a.packed = packed;
+  a.N = N;
+  a.K = K;
+  a.kind = kind;
+  a.head_dim = head_dim;
+  a.batch = batch;
+  a.x = x;
+  a.norm_gain = norm_gain;
+  a.eps = eps;
+  a.bias = bias;
+  a.y = y;
+  a.epi = epi;
+  hipError_t e = launch_gemv(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "nq_gemv_w4a16 launch");
+  return NQ_OK;
+}
+
+nq_status nq_unpack_weights_dev(const void* packed_dev, int32_t N, int32_t K, int32_t group,
+                                nq_mat_kind kind, int32_t head_dim, int8_t* q_out_dev, uint16_t* s_out_dev,
+                                void* stream) {
+  nq_status st = check_pack_args(N, K, group, kind, head_dim);
+  if (st != NQ_OK) return st;
+  if (!packed_dev || !q_out_dev || !s_out_dev) return fail(NQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(packed_dev)) return fail(NQ_ERR_INVALID_ARG, "packed must be 16-byte aligned");
+  hipError_t e = launch_unpack_dev(packed_dev, N, K, kind, head_dim, q_out_dev, s_out_dev,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "unpack launch");
+  return NQ_OK;
+}
+
+size_t nq_kv_pool_bytes(const nq_config* cfg, int32_t num_pages) {
+  if (nq_config_check(cfg) != NQ_OK || num_pages <= 0) return 0;
+  return static_cast<size_t>(cfg->layers) * 2 * layer_pool_elems(*cfg, num_pages) * 2;
+}
+
+nq_status nq_kv_alloc(const nq_config* cfg, void* pool_dev, size_t bytes, int32_t num_pages, nq_kv** out) {
+  nq_status st = nq_config_check(cfg);
+  if (st != NQ_OK) return st;
+  if (!pool_dev || !out) return fail(NQ_ERR_INVALID_ARG, "nq_kv_alloc: null pool or out");
+  if (num_pages <= 0) return fail(NQ_ERR_INVALID_ARG, "num_pages must be positive");
+  if (!aligned16(pool_dev)) return fail(NQ_ERR_INVALID_ARG, "pool must be 16-byte aligned");
+  if (bytes < nq_kv_pool_bytes(cfg, num_pages))
+    return fail(NQ_ERR_INVALID_ARG, "pool too small: %zu < %zu", bytes, nq_kv_pool_bytes(cfg, num_pages));
+  nq_kv* kv = new nq_kv;
+  kv->cfg = *cfg;
+  kv->pool = pool_dev;
+  kv->bytes = bytes;
+  kv->num_pages = num_pages;
+  *out = kv;
+  return NQ_OK;
+}
+
+void nq_kv_free(nq_kv* kv) { delete kv; }
+
+nq_status nq_kv_append(nq_kv* kv, int32_t layer, int32_t batch, const int32_t* page_table, int32_t max_pages,
+                       const int32_t* pos, const void* k, const void* v, int32_t* err_flag, void* stream) {
+  if (!kv) return fail(NQ_ERR_INVALID_ARG, "null kv");
+  if (layer < 0 || layer >= kv->cfg.layers) return fail(NQ_ERR_OUT_OF_RANGE, "layer %d out of range", layer);
+  if (batch < 1) return fail(NQ_ERR_INVALID_ARG, "batch must be >= 1");
+  if (max_pages < 1) return fail(NQ_ERR_INVALID_ARG, "max_pages must be >= 1");
+  if (!page_table || !pos || !k || !v) return fail(NQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(k) || !aligned16(v)) return fail(NQ_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  const size_t lp = layer_pool_elems(kv->cfg, kv->num_pages);
+  uint16_t* kb = static_cast<uint16_t*>(kv->pool) + static_cast<size_t>(layer) * 2 * lp;
+  hipError_t e = launch_kv_append(kb, kb + lp, batch, kv->cfg.n_kv_heads, kv->cfg.head_dim, page_table, max_pages,
+                                  kv->num_pages, pos, k, v, err_flag, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kv append launch");
+  return NQ_OK;
+}
+
+size_t nq_attn_workspace_bytes(const nq_config* cfg, int32_t batch, int32_t max_pages) {
+  if (nq_config_check(cfg) != NQ_OK || batch < 1 || max_pages < 1) return 0;
+  const int S = attn_splits_for(max_pages);
+  return align256(static_cast<size_t>(batch) * cfg->n_heads * S * cfg->head_dim * 4) +
+         align256(static_cast<size_t>(batch) * cfg->n_heads * S * 2 * 4);
+}
+
+nq_status nq_attn_decode(const nq_kv* kv, int32_t layer, int32_t batch, const void* q, const int32_t* page_table,
+                         int32_t max_pages, const int32_t* lens, void* out, void* workspace, size_t ws_bytes,
+                         int32_t* err_flag, void* stream) {
+  if (!kv) return fail(NQ_ERR_INVALID_ARG, "null kv");
+  if (layer < 0 || layer >= kv->cfg.layers) return fail(NQ_ERR_OUT_OF_RANGE, "layer %d out of range", layer);
+  if (batch < 1) return fail(NQ_ERR_INVALID_ARG, "batch must be >= 1");
+  if (max_pages < 1) return fail(NQ_ERR_INVALID_ARG, "max_pages must be >= 1");
+  if (!q || !page_table || !lens || !out || !workspace)
+    return fail(NQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(q) || !aligned16(workspace)) return fail(NQ_ERR_INVALID_ARG, "q and workspace must be 16-byte aligned");
+  if (ws_bytes < nq_attn_workspace_bytes(&kv->cfg, batch, max_pages))
+    return fail(NQ_ERR_INVALID_ARG, "attention workspace too small");
+  const size_t lp = layer_pool_elems(kv->cfg, kv->num_pages);
+  const uint16_t* kb = static_cast<const uint16_t*>(kv->pool) + static_cast<size_t>(layer) * 2 * lp;
+  AttnArgs a{};
+  a.q = q;
+  a.k_pool = kb;
+  a.v_pool = kb + lp;
+  a.page_table = page_table;
+  a.max_pages = max_pages;
+  a.num_pages = kv->num_pages;
+  a.lens = lens;
+  a.len_add = 0;
+  a.out = out;
+  a.batch = batch;
+  a.n_heads = kv->cfg.n_heads;
+  a.n_kv = kv->cfg.n_kv_heads;
+  a.head_dim = kv->cfg.head_dim;
+  a.splits = attn_splits_for(max_pages);
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                       align256(static_cast<size_t>(batch) * a.n_heads * a.splits * a.head_dim * 4));
+  a.err = err_flag;
+  hipError_t e = launch_attention(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return NQ_OK;
+}
+
+nq_status nq_model_create(const nq_config* cfg, nq_model** out) {
+  nq_status st = nq_config_check(cfg);
+  if (st != NQ_OK) return st;
+  if (!out) return fail(NQ_ERR_INVALID_ARG, "null out");
+  nq_model* m = new nq_model;
+  m->cfg = *cfg;
+  m->layers.assign(cfg->layers, nq_layer_ptrs{});
+  m->bound.assign(cfg->layers, 0);
+  *out = m;
+  return NQ_OK;
+}
+
+nq_status nq_model_bind_layer(nq_model* m, int32_t layer, const nq_layer_ptrs* p) {
+  if (!m || !p) return fail(NQ_ERR_INVALID_ARG, "null model or pointers");
+  if (layer < 0 || layer >= m->cfg.layers) return fail(NQ_ERR_OUT_OF_RANGE, "layer %d out of range", layer);
+  const void* req[] = {p->qkv_packed, p->qkv_bias, p->o_packed, p->gate_up_packed, p->down_packed,
+                       p->attn_norm, p->mlp_norm};
+  for (const void* q : req) {
+    if (!q) return fail(NQ_ERR_INVALID_ARG, "layer %d: null pointer", layer);
+    if (!aligned16(q)) return fail(NQ_ERR_INVALID_ARG, "layer %d: pointer not 16-byte aligned", layer);
+  }
+  m->layers[layer] = *p;
+  m->bound[layer] = 1;
+  return NQ_OK;
+}
+
+nq_status nq_model_bind_head(nq_model* m, const void* embed, const void* final_norm, const void* lm_packed) {
+  if (!m || !embed || !final_norm || !lm_packed) return fail(NQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(embed) || !aligned16(final_norm) || !aligned16(lm_packed))
+    return fail(NQ_ERR_INVALID_ARG, "head pointers must be 16-byte aligned");
+  m->embed = embed;
+  m->final_norm = final_norm;
+  m->lm = lm_packed;
+  return NQ_OK;
+}
+
+nq_status nq_model_bind_rope(nq_model* m, const void* rope) {
+  if (!m || !rope) return fail(NQ_ERR_INVALID_ARG, "null pointer");
+  m->rope = static_cast<const float*>(rope);
+  return NQ_OK;
+}
+
+size_t nq_workspace_bytes(const nq_config* cfg, int32_t batch, int32_t max_pages) {
+  if (nq_config_check(cfg) != NQ_OK || batch < 1 || batch > cfg->max_batch || max_pages < 1) return 0;
+  return carve(*cfg, batch, max_pages, nullptr).total;
+}
+
+nq_status nq_model_bind_workspace(nq_model* m, void* ws, size_t bytes) {
+  if (!m || !ws) return fail(NQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(ws)) return fail(NQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  m->ws = ws;
+  m->ws_bytes = bytes;
+  return NQ_OK;
+}
+
+void nq_model_destroy(nq_model* m) { delete m; }
+
+nq_status nq_decode_step(nq_model* m, nq_kv* kv, const nq_step_io* io, void* stream) {
+  nq_status st = check_model_ready(m, kv, io);
+  if (st != NQ_OK) return st;
+  if (enqueue_step(m, kv, io, static_cast<hipStream_t>(stream)) < 0) return NQ_ERR_HIP;
+  return NQ_OK;
+}
+
+nq_status nq_graph_capture(nq_model* m, nq_kv* kv, const nq_step_io* io, void* stream, nq_graph** out) {
+  nq_status st = check_model_ready(m, kv, io);
+  if (st != NQ_OK) return st;
+  if (!out) return fail(NQ_ERR_INVALID_ARG, "null out");
+  if (!stream) return fail(NQ_ERR_STATE, "cannot capture the null stream");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &cs);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone) return fail(NQ_ERR_STATE, "stream is already capturing");
+  if ((e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal)) != hipSuccess)
+    return hip_fail(e, "hipStreamBeginCapture");
+  const int n = enqueue_step(m, kv, io, s);
+  hipGraph_t g = nullptr;
+  hipError_t e2 = hipStreamEndCapture(s, &g);
+  if (n < 0) {
+    if (g) (void)hipGraphDestroy(g);
+    return NQ_ERR_HIP;
+  }
+  if (e2 != hipSuccess) return hip_fail(e2, "hipStreamEndCapture");
+  hipGraphExec_t ex = nullptr;
+  if ((e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0)) != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return hip_fail(e, "hipGraphInstantiate");
+  }
+  nq_graph* gr = new nq_graph;
+  gr->graph = g;
+  gr->exec = ex;
+  gr->kernels = n;
+  *out = gr;
+  return NQ_OK;
+}
+
+nq_status nq_graph_launch(nq_graph* g, void* stream) {
+  if (!g) return fail(NQ_ERR_INVALID_ARG, "null graph");
+  hipError_t e = hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+  return NQ_OK;
+}
+
+int32_t nq_graph_kernel_count(const nq_graph* g) { return g ? g->kernels : -1; }
+
+void nq_graph_destroy(nq_graph* g) {
+  if (!g) return;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  delete g;
+}
+
+nq_status nq_check_device_error(int32_t* err_flag_dev, void* stream) {
+  if (!err_flag_dev) return fail(NQ_ERR_INVALID_ARG, "null err flag");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  int32_t v = 0;
+  if ((e = hipMemcpy(&v, err_flag_dev, sizeof v, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "reading err flag");
+  if (v != 0) {
+    const int32_t zero = 0;
+    if ((e = hipMemcpy(err_flag_dev, &zero, sizeof zero, hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_fail(e, "resetting err flag");
+    return fail(NQ_ERR_DEVICE_FAULT, "device error flag 0x%x (1 KV write, 2 attention read, 4 token id, 8 NaN logits)", v);
+  }
+  return NQ_OK;
+}
+
+}  // extern "C"

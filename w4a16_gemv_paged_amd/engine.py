@@ -1,0 +1,190 @@
+"""Device-memory plumbing around libnq for a whole model.
+
+Packs host parameters with ``nq_pack_weights`` (C++), uploads them into torch
+tensors, binds them to an ``nq_model``, owns the KV pool, the workspace and the
+per-step buffers, and drives decode steps (eager or as graph replays). PyTorch
+is used only to allocate device memory, copy host data in and out and pick the
+stream; every arithmetic step runs in libnq.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import (NQConfig, NQLayerPtrs, NQStepIO, NQ_MAT_PLAIN, NQ_MAT_QKV, NQ_MAT_GATE_UP, NQ_MAT_LM_HEAD,
+               nq_pack_weights, nq_model_create, nq_model_bind_layer, nq_model_bind_head, nq_model_bind_rope,
+               nq_rope_table_fill, nq_workspace_bytes, nq_model_bind_workspace, nq_model_destroy,
+               nq_kv_pool_bytes, nq_kv_alloc, nq_kv_free, nq_decode_step, nq_graph_capture, nq_graph_launch,
+               nq_graph_destroy, nq_graph_kernel_count, nq_check_device_error)
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device, non_blocking=False)
+
+
+def _f16_dev(a, device):
+    return to_device(np.asarray(a, np.float16).view(np.int16), device)
+
+
+class DeviceModel:
+    """A Qwen2-style decoder bound to libnq.
+
+    ``layer_params(l)`` returns the parameter dict of layer l (float32
+    wq/wk/wv/wo/wg/wu/wd, float16 bq/bk/bv/g1/g2); ``head`` holds float16
+    embed/g_final and float32 lm_head. Host copies are dropped after upload."""
+
+    def __init__(self, shape, layer_params, head: dict, max_batch: int, max_pos: int, device="cuda"):
+        self.shape = shape
+        self.device = device
+        self.cfg = NQConfig.from_shape(shape, max_batch, max_pos)
+        self.handle = nq_model_create(self.cfg)
+        self._keep = []
+        d = shape.head_dim
+        for li in range(shape.layers):
+            p = layer_params(li)
+            qkv = nq_pack_weights(np.concatenate([p["wq"], p["wk"], p["wv"]]), NQ_MAT_QKV, d)
+            o = nq_pack_weights(p["wo"], NQ_MAT_PLAIN)
+            gu = nq_pack_weights(np.concatenate([p["wg"], p["wu"]]), NQ_MAT_GATE_UP)
+            dn = nq_pack_weights(p["wd"], NQ_MAT_PLAIN)
+            bias = np.concatenate([p["bq"], p["bk"], p["bv"]]).astype(np.float16)
+            ts = [to_device(qkv, device), _f16_dev(bias, device), to_device(o, device), to_device(gu, device),
+                  to_device(dn, device), _f16_dev(p["g1"], device), _f16_dev(p["g2"], device)]
+            self._keep.extend(ts)
+            nq_model_bind_layer(self.handle, li, NQLayerPtrs(*[t.data_ptr() for t in ts]))
+            del p, qkv, o, gu, dn
+        self.embed = _f16_dev(head["embed"], device)
+        self.g_final = _f16_dev(head["g_final"], device)
+        self.lm = to_device(nq_pack_weights(head["lm_head"], NQ_MAT_LM_HEAD), device)
+        nq_model_bind_head(self.handle, self.embed, self.g_final, self.lm)
+        self.rope = to_device(nq_rope_table_fill(self.cfg), device)
+        nq_model_bind_rope(self.handle, self.rope)
+        self.ws = None
+
+    def weight_bytes(self) -> int:
+        n = sum(t.numel() * t.element_size() for t in self._keep)
+        return n + self.lm.numel() + self.embed.numel() * 2 + self.g_final.numel() * 2
+
+    def close(self):
+        if self.handle:
+            nq_model_destroy(self.handle)
+            self.handle = None
+
+
+class KVCache:
+    """A caller-owned KV pool of ``num_pages`` pages (optionally NaN-poisoned)."""
+
+    def __init__(self, model: DeviceModel, num_pages: int, poison: bool = True):
+        self.num_pages = num_pages
+        nbytes = nq_kv_pool_bytes(model.cfg, num_pages)
+        self.pool = torch.empty(nbytes // 2, dtype=torch.int16, device=model.device)
+        self.pool.fill_(0x7E00 if poison else 0)  # fp16 NaN bits
+        self.handle = nq_kv_alloc(model.cfg, self.pool, nbytes, num_pages)
+
+    def view(self, cfg: NQConfig) -> torch.Tensor:
+        """The pool as fp16 [layer][2][page][kv_head][16][head_dim] (bit view)."""
+        return self.pool.view(torch.float16).view(cfg.layers, 2, self.num_pages, cfg.n_kv_heads, 16, cfg.head_dim)
+
+    def close(self):
+        if self.handle:
+            nq_kv_free(self.handle)
+            self.handle = None
+
+
+class Stepper:
+    """Per-step device buffers for a batch and the io struct that points at them."""
+
+    def __init__(self, model: DeviceModel, kv: KVCache, page_table: np.ndarray, hist_len: int = 0,
+                 want_logits: bool = False, want_layers: bool = False):
+        dev = model.device
+        cfg = model.cfg
+        self.model, self.kv = model, kv
+        self.batch, self.max_pages = page_table.shape
+        self.page_table = to_device(page_table.astype(np.int32), dev)
+        self.tokens = torch.zeros(self.batch, dtype=torch.int32, device=dev)
+        self.pos = torch.zeros(self.batch, dtype=torch.int32, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.logits = torch.empty(self.batch, cfg.vocab, dtype=torch.float32, device=dev) if want_logits else None
+        self.layer_out = (torch.empty(cfg.layers, self.batch, cfg.hidden, dtype=torch.float16, device=dev)
+                          if want_layers else None)
+        self.hist = torch.full((self.batch, hist_len), -1, dtype=torch.int32, device=dev) if hist_len else None
+        wsb = nq_workspace_bytes(cfg, self.batch, self.max_pages)
+        self.ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+        nq_model_bind_workspace(model.handle, self.ws, wsb)
+        p = lambda t: t.data_ptr() if t is not None else None
+        self.io = NQStepIO(self.batch, self.max_pages, p(self.page_table), p(self.tokens), p(self.pos),
+                           p(self.logits), p(self.layer_out), p(self.hist), hist_len, p(self.err))
+        self.graph = None
+
+    def set_tokens(self, toks, stream=None):
+        self.tokens.copy_(torch.as_tensor(np.asarray(toks, np.int32)), non_blocking=False)
+
+    def set_pos(self, pos):
+        self.pos.copy_(torch.as_tensor(np.asarray(pos, np.int32)), non_blocking=False)
+
+    def step(self, stream=None):
+        nq_decode_step(self.model.handle, self.kv.handle, self.io, stream)
+
+    def capture(self, stream):
+        self.graph = nq_graph_capture(self.model.handle, self.kv.handle, self.io, stream)
+        return nq_graph_kernel_count(self.graph)
+
+    def replay(self, stream):
+        nq_graph_launch(self.graph, stream)
+
+    def check(self, stream=None):
+        nq_check_device_error(self.err, stream)
+
+    def close(self):
+        if self.graph:
+            nq_graph_destroy(self.graph)
+            self.graph = None
+
+
+def run_greedy(st: Stepper, prompts, n_gen: int, use_graph: bool = False, stream=None,
+               record_logits: bool = False, record_layers: bool = False):
+    """Greedy decode of ``batch`` sequences in lockstep, one token per step.
+
+    prompts: list of int sequences (ragged allowed). Sequence b goes through its
+    prompt at positions 0..P_b-1, then generates n_gen tokens, feeding each
+    back (the cache ends at P_b + n_gen - 1 positions). Sequences whose prompt
+    is shorter start generating earlier and stop after n_gen tokens; they keep
+    stepping (their extra tokens are ignored) until every sequence is done.
+    Returns generated tokens [B][n_gen] and, if asked, the logits / layer
+    outputs seen at every step."""
+    B = st.batch
+    P = [len(p) for p in prompts]
+    total = max(P) + n_gen - 1
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    gen = [[] for _ in range(B)]
+    logits, layers = [], []
+    cur = np.array([p[0] for p in prompts], np.int32)
+    st.set_pos(np.zeros(B, np.int32))
+    st.set_tokens(cur)
+    if use_graph and st.graph is None:
+        st.capture(stream)
+    for s in range(total):
+        if use_graph:
+            st.replay(stream)
+        else:
+            st.step(stream)
+        nxt = st.tokens.cpu().numpy()
+        if record_logits:
+            logits.append(st.logits.cpu().numpy().copy())
+        if record_layers:
+            layers.append(st.layer_out.cpu().numpy().copy())
+        for b in range(B):
+            if s >= P[b] - 1 and len(gen[b]) < n_gen:
+                gen[b].append(int(nxt[b]))
+            cur[b] = prompts[b][s + 1] if s + 1 < P[b] else nxt[b]
+        st.set_tokens(cur)
+    st.check(stream)
+    out = {"tokens": np.array(gen, np.int64)}
+    if record_logits:
+        out["logits"] = np.array(logits)
+    if record_layers:
+        out["layer_out"] = np.array(layers)
+    return out

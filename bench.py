@@ -1,0 +1,412 @@
+#!/usr/bin/env python3
+"""Decode benchmark of libnq on one MI355X: a Qwen2.5-Coder-7B-shaped model
+with symmetric group-128 INT4 weights (fp16 scales) and fp16 activations,
+random-init (synthetic) weights and prompts.
+
+Headline (the printed JSON line): batch-1 greedy decode, 512-token random
+prompt fed through the step, then the step replayed as one HIP graph per token;
+``value`` = tokens/s over exactly --steps timed replays (after --warmup).
+The same line also carries the batch-8 decode (ragged contexts uniform in
+[128, 16384], 128 steps), the W4A16 GEMV sweep at the 7B projection shapes
+(GB/s and fraction of the 8 TB/s HBM peak), the roofline of the dominant
+kernel (the gate/up GEMV + SwiGLU) and the CPU oracle timed on a bounded
+sample.
+
+Modes (for profiling runs): --mode roofline launches only the gate/up GEMV of
+28 distinct weight copies; --mode copy runs a 1 GiB device copy (the
+calibration for the FETCH_SIZE / WRITE_SIZE counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode ms/token & tok/s (7B INT4, B=1/8); GEMV HBM GB/s as % of peak"
+PEAK_HBM = 8.0e12
+GEMV_ROTATION = {(3584, 4608): 64, (3584, 3584): 82, (3584, 37888): 8, (18944, 3584): 16}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_gate_up_swiglu_7b_b1_pmc.md")
+KERNEL_SRC = os.path.join(ROOT, "w4a16_gemv_paged_amd", "csrc", "kernels.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def gemv_bytes(k: int, n: int, b: int) -> int:
+    """Algorithmic bytes of one W4A16 GEMV: INT4 codes + fp16 scales + fp16 in/out."""
+    return k * n // 2 + k * n // 64 + 2 * b * (k + n)
+
+
+def step_weight_bytes(shape) -> int:
+    """Bytes one B=1 decode step must stream: packed weights, biases and norm
+    gains of every layer, the LM head, the final gain and one embedding row."""
+    H, I, nh, nkv, d, V = (shape.hidden, shape.intermediate, shape.n_heads, shape.n_kv_heads, shape.head_dim,
+                           shape.vocab)
+    qkv_n = (nh + 2 * nkv) * d
+    pk = lambda n, k: n * k // 2 + n * (k // 128) * 2
+    layer = pk(qkv_n, H) + 2 * qkv_n + pk(H, nh * d) + pk(2 * I, H) + pk(H, I) + 2 * 2 * H
+    return shape.layers * layer + pk(V, H) + 2 * H + 2 * H
+
+
+def kernel_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM traffic per gate/up launch from the committed PMC summary, if it was
+    taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    m = re.search(r"TRAFFIC_JSON:\s*(\{.*\})", open(TRAFFIC_FILE).read())
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("kernel_sha") != kernel_sha():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def time_launches(fn, launches: int, stream, reps: int = 1):
+    """Per-launch durations from HIP events recorded around each launch on
+    ``stream``; returns (mean seconds per launch, back-to-back seconds per launch)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches * reps)]
+    stream.synchronize()
+    i = 0
+    for _ in range(reps):
+        for j in range(launches):
+            evs[i][0].record(stream)
+            fn(j)
+            evs[i][1].record(stream)
+            i += 1
+    stream.synchronize()
+    per = [a.elapsed_time(b) * 1e-3 for a, b in evs]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        for j in range(launches):
+            fn(j)
+    e1.record(stream)
+    stream.synchronize()
+    return sum(per) / len(per), e0.elapsed_time(e1) * 1e-3 / (launches * reps)
+
+
+def gate_up_roofline(layers, hidden: int, inter: int, stream, reps: int = 10):
+    """Times the gate/up GEMV + SwiGLU launch of the decode step (B=1, RMSNorm
+    prologue) over the given per-layer (packed, gain) pairs."""
+    import numpy as np
+    import torch
+    import synth
+    import w4a16_gemv_paged_amd as nq
+    x = torch.from_numpy(synth.activations(1, hidden, seed=1).view(np.int16)).cuda()
+    y = torch.empty(1, inter, dtype=torch.float16, device="cuda")
+    sid = stream.cuda_stream
+
+    def launch(j):
+        packed, gain = layers[j % len(layers)]
+        nq.nq_gemv_w4a16(packed, 2 * inter, hidden, nq.NQ_MAT_GATE_UP, 0, 1, x, gain, 1e-6, None, y,
+                         nq.NQ_EPI_SWIGLU_F16, sid)
+
+    for j in range(len(layers)):
+        launch(j)
+    mean_s, b2b_s = time_launches(launch, len(layers), stream, reps)
+    unit_bytes = gemv_bytes(hidden, 2 * inter, 1)
+    traffic = read_traffic()
+    return {
+        "kernel": "gemv_w4a16_kernel<1, SWIGLU> (gate/up GEMV + SwiGLU, RMSNorm prologue), K=3584 N=37888 B=1",
+        "bound": "hbm", "achieved": round(unit_bytes / mean_s / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
+        "frac": round(unit_bytes / mean_s / PEAK_HBM, 4),
+        "traffic": traffic,
+        "algorithmic_bytes_per_launch": unit_bytes,
+        "mean_launch_us": round(mean_s * 1e6, 3),
+        "back_to_back_us": round(b2b_s * 1e6, 3),
+        "launches_timed": len(layers) * reps,
+    }
+
+
+def gemv_sweep(stream):
+    import numpy as np
+    import torch
+    import synth
+    import w4a16_gemv_paged_amd as nq
+    out = []
+    sid = stream.cuda_stream
+    for (k, n), copies in GEMV_ROTATION.items():
+        packed = nq.nq_pack_weights(synth.gemv_weight(k, n, seed=0))
+        bufs = [torch.from_numpy(packed).cuda() for _ in range(copies)]  # >= 512 MB of distinct addresses
+        for b in (1, 4):
+            x = torch.from_numpy(synth.activations(b, k, seed=1).view(np.int16)).cuda()
+            y = torch.empty(b, n, dtype=torch.float16, device="cuda")
+            fn = lambda j: nq.nq_gemv_w4a16(bufs[j], n, k, 0, 0, b, x, None, 1e-6, None, y, 0, sid)
+            for j in range(copies):
+                fn(j)
+            mean_s, b2b_s = time_launches(fn, copies, stream, reps=max(1, 256 // copies))
+            nb = gemv_bytes(k, n, b)
+            out.append({"K": k, "N": n, "B": b, "bytes": nb, "us": round(mean_s * 1e6, 2),
+                        "GBs": round(nb / mean_s / 1e9, 1), "frac": round(nb / mean_s / PEAK_HBM, 4),
+                        "back_to_back_us": round(b2b_s * 1e6, 2)})
+            log(f"gemv K={k} N={n} B={b}: {mean_s * 1e6:.2f} us {nb / mean_s / 1e9:.0f} GB/s")
+        del bufs
+    agg = {}
+    for b in (1, 4):
+        rows = [r for r in out if r["B"] == b]
+        tb = sum(r["bytes"] for r in rows)
+        tt = sum(r["bytes"] / (r["GBs"] * 1e9) for r in rows)
+        agg[f"B{b}"] = {"GBs": round(tb / tt / 1e9, 1), "frac": round(tb / tt / PEAK_HBM, 4)}
+    return out, agg
+
+
+def cpu_baseline(shape, head, sample_layers: int = 2, steps: int = 4, ctx: int = 512):
+    """The oracle's decode step timed on the host cores on a bounded sample:
+    ``sample_layers`` of the 28 layers plus the full LM head, at context ``ctx``
+    with a synthetic (random) contiguous cache, scaled to the full model."""
+    import numpy as np
+    import synth
+    import oracle
+    from oracle.model import Dims, OracleLayer, OracleHead, ContiguousKV, layer_decode, head_logits, OracleModel
+    cores = len(os.sched_getaffinity(0))
+    dims = Dims(shape.hidden, shape.intermediate, shape.n_heads, shape.n_kv_heads, shape.head_dim, shape.vocab,
+                shape.rms_eps, shape.rope_theta)
+    t0 = time.time()
+    layers = [OracleLayer(synth.layer_params(shape, i, seed=0)) for i in range(sample_layers)]
+    for L in layers:
+        for nm in ("qkv", "o", "gu", "d"):
+            L.w(nm)
+    oh = OracleHead(head)
+    oh.w_lm()
+    model = OracleModel(dims, layers, oh)
+    rng = np.random.default_rng(9)
+    cache = ContiguousKV(sample_layers, shape.n_kv_heads, shape.head_dim)
+    for li in range(sample_layers):
+        cache.k[li] = rng.standard_normal((ctx, shape.n_kv_heads, shape.head_dim)).astype(np.float16)
+        cache.v[li] = rng.standard_normal((ctx, shape.n_kv_heads, shape.head_dim)).astype(np.float16)
+    setup = time.time() - t0
+    t_layers, t_head = [], []
+    tok = 17
+    for s in range(steps):
+        pos = ctx + s
+        h = oh.embed[tok]
+        t1 = time.perf_counter()
+        for li, L in enumerate(layers):
+            h = layer_decode(L, dims, h, pos, lambda k, v, li=li: cache.append(li, pos, k, v),
+                             lambda n, li=li: cache.get(li, n))
+        t2 = time.perf_counter()
+        z = head_logits(model, h)
+        tok = oracle.argmax_lowest(z)
+        t3 = time.perf_counter()
+        t_layers.append((t2 - t1) / sample_layers)
+        t_head.append(t3 - t2)
+    per_layer = sorted(t_layers)[len(t_layers) // 2]
+    per_head = sorted(t_head)[len(t_head) // 2]
+    per_token = per_layer * shape.layers + per_head
+    return {"value": round(1.0 / per_token, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": (f"oracle decode_step (NumPy float64, dequantised weights cached) on {sample_layers} of "
+                       f"{shape.layers} layers + full LM head, context {ctx} with a synthetic contiguous cache, "
+                       f"median of {steps} steps; per-token time = median layer time x {shape.layers} + head time"),
+            "s_per_token": round(per_token, 3), "setup_s": round(setup, 1)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=248)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--mode", choices=["full", "roofline", "copy"], default="full")
+    ap.add_argument("--skip-b8", action="store_true")
+    ap.add_argument("--skip-sweep", action="store_true")
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--b8-steps", type=int, default=128)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (the decode step runs on a single MI355X; there is "
+              "no multi-GPU mode). Run it with --gpus 1.", file=sys.stderr, flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+    import synth
+    import w4a16_gemv_paged_amd as nq
+    from w4a16_gemv_paged_amd.engine import DeviceModel, KVCache, Stepper
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    shape = synth.QWEN7B
+
+    if args.mode == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n}), flush=True)
+        return 0
+
+    if args.mode == "roofline":
+        packed = nq.nq_pack_weights(np.concatenate([synth.gemv_weight(3584, 18944, seed=0, copy=1),
+                                                    synth.gemv_weight(3584, 18944, seed=0, copy=2)]),
+                                    nq.NQ_MAT_GATE_UP)
+        gain = torch.from_numpy((1 + 0.02 * np.random.default_rng(3).standard_normal(3584))
+                                .astype(np.float16).view(np.int16)).cuda()
+        layers = [(torch.from_numpy(packed).cuda(), gain) for _ in range(shape.layers)]
+        with torch.cuda.stream(stream):
+            r = gate_up_roofline(layers, shape.hidden, shape.intermediate, stream, reps=4)
+        print(json.dumps({"mode": "roofline", "roofline": r}), flush=True)
+        return 0
+
+    # ------------------------------------------------------------------ model
+    t0 = time.time()
+    log("drawing and packing the 7B-shaped weights")
+    head = synth.head_params(shape, seed=0)
+    dm = DeviceModel(shape, lambda l: synth.layer_params(shape, l, seed=0), head, max_batch=8, max_pos=32768)
+    torch.cuda.synchronize()
+    log(f"model ready in {time.time() - t0:.1f} s ({dm.weight_bytes() / 1e9:.2f} GB on device)")
+
+    # ------------------------------------------------------------------ B = 1
+    P = 512
+    W, K = args.warmup, args.steps
+    prompt = synth.prompt_ids(P, shape.vocab, seed=2)
+    need = P + W + K + 64
+    max_pages = (need + 15) // 16
+    pt, total = synth.decode_page_tables(1, max_pages, seed=3)
+    kv1 = KVCache(dm, total, poison=False)
+    st = Stepper(dm, kv1, pt, hist_len=need + 1)
+    with torch.cuda.stream(stream):
+        st.set_pos([0])
+        st.set_tokens([prompt[0]])
+        n_kernels = st.capture(stream)
+        log(f"captured the step: {n_kernels} kernels")
+        for i in range(P):                      # prompt, one token per replay
+            st.replay(stream)
+            if i + 1 < P:
+                st.set_tokens([prompt[i + 1]])
+        for _ in range(W):
+            st.replay(stream)
+        torch.cuda.synchronize()
+        ctx0 = P + W
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t1 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(K):
+            st.replay(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t1
+        ms_b1 = wall * 1e3 / K
+        ms_b1_events = e0.elapsed_time(e1) / K
+        st.check(stream)
+        # eager launches of the same step (the pages' eager vs graph comparison)
+        ne = 16
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(ne):
+            st.step(stream)
+        torch.cuda.synchronize()
+        ms_eager = (time.perf_counter() - t2) * 1e3 / ne
+        st.check(stream)
+    hist = st.hist.cpu().numpy()[0]
+    gen = hist[P:P + W + K]
+    log(f"B=1: {ms_b1:.3f} ms/token ({1e3 / ms_b1:.1f} tok/s), eager {ms_eager:.3f} ms/token; "
+        f"first tokens {gen[:8].tolist()}")
+    st.close()
+    kv1.close()
+    del st, kv1
+
+    # ------------------------------------------------------------------ roofline of the dominant kernel
+    with torch.cuda.stream(stream):
+        roof = gate_up_roofline([(L["gate_up"], L["g2"]) for L in dm.layers], shape.hidden, shape.intermediate,
+                                stream, reps=10)
+    log(f"gate/up GEMV: {roof['mean_launch_us']} us/launch, {roof['achieved']} GB/s ({roof['frac'] * 100:.1f}%)")
+
+    # ------------------------------------------------------------------ B = 8
+    b8 = None
+    if not args.skip_b8:
+        lens = synth.ragged_lengths(8, 128, 16384, seed=4)
+        max_pages8 = 2048
+        pt8, total8 = synth.decode_page_tables(8, max_pages8, seed=3)
+        kv8 = KVCache(dm, total8, poison=False)
+        synth.fill_device_normal(kv8.pool.view(torch.float16), seed=7)
+        st8 = Stepper(dm, kv8, pt8)
+        with torch.cuda.stream(stream):
+            st8.set_pos(lens)
+            st8.set_tokens(synth.prompt_ids(8, shape.vocab, seed=8))
+            st8.capture(stream)
+            for _ in range(4):
+                st8.replay(stream)
+            torch.cuda.synchronize()
+            ctx_start = (lens + 4).tolist()
+            t3 = time.perf_counter()
+            for _ in range(args.b8_steps):
+                st8.replay(stream)
+            torch.cuda.synchronize()
+            ms8 = (time.perf_counter() - t3) * 1e3 / args.b8_steps
+            st8.check(stream)
+        mean_ctx = float(np.mean(lens)) + 4 + args.b8_steps / 2
+        kv_bytes = 2 * shape.layers * shape.n_kv_heads * shape.head_dim * 2 * mean_ctx * 8
+        w_bytes = step_weight_bytes(shape)
+        b8 = {"ms_per_step": round(ms8, 4), "tok_s": round(8e3 / ms8, 1), "steps": args.b8_steps,
+              "context_at_start": ctx_start, "mean_context": round(mean_ctx, 1),
+              "bytes_per_step": int(w_bytes + kv_bytes),
+              "hbm_frac": round((w_bytes + kv_bytes) / (ms8 * 1e-3) / PEAK_HBM, 4)}
+        log(f"B=8: {ms8:.3f} ms/step ({8e3 / ms8:.1f} tok/s)")
+        st8.close()
+        kv8.close()
+        del st8, kv8
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------ GEMV sweep
+    sweep, agg = (None, None)
+    if not args.skip_sweep:
+        with torch.cuda.stream(stream):
+            sweep, agg = gemv_sweep(stream)
+    dm.close()
+    del dm
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------ CPU oracle
+    cpu = None
+    if not args.skip_cpu:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(shape, head)
+        log(f"oracle: {cpu['s_per_token']} s/token on {cpu['cores']} cores")
+
+    wb = step_weight_bytes(shape)
+    res = {
+        "metric": METRIC, "value": round(1e3 / ms_b1, 2), "unit": "tok/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_b1, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "Qwen2.5-Coder-7B-shaped greedy decode, batch 1, 512-token random prompt, "
+                               "step replayed as one HIP graph", "batch": 1, "prompt_tokens": P,
+                   "context_during_timing": [ctx0, ctx0 + K], "weights": "int4 symmetric g128, fp16 scales",
+                   "activations": "fp16, fp32 accumulation", "kernels_per_step": n_kernels},
+        "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "cpu_baseline": cpu,
+        "ms_per_token_b1_events": round(ms_b1_events, 4),
+        "ms_per_token_b1_eager": round(ms_eager, 4),
+        "step_weight_bytes": wb,
+        "step_roofline_ms": round(wb / PEAK_HBM * 1e3, 4),
+        "step_roofline_frac": round(wb / PEAK_HBM * 1e3 / ms_b1, 4),
+        "dominant_kernel": roof,
+        "b8": b8,
+        "gemv_sweep": sweep, "gemv_aggregate": agg,
+        "context": {"pages_h100_ms_per_token_graph": 16.7, "pages_h100_ms_per_token_eager": 119,
+                    "pages_h100_tok_s": 60},
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -235,7 +235,8 @@ size_t nq_attn_workspace_bytes(const nq_config* cfg, int32_t batch, int32_t max_
  * are never used, whatever they hold.
  * q: device fp16 [batch][n_heads][head_dim]; out: device fp16, same shape.
  * lens: device int32 [batch] (0 gives a zero output row).
- * workspace: device, nq_attn_workspace_bytes(cfg, batch, max_pages) bytes.
+ * workspace: device, nq_attn_workspace_bytes(cfg, batch, max_pages) bytes for
+ * the split partials; calls that share a workspace must not overlap.
  * err_flag: optional device int32 (bad page id or length -> ORs 2, output 0).
  */
 nq_status nq_attn_decode(const nq_kv* kv, int32_t layer, int32_t batch, const void* q,
@@ -304,7 +305,9 @@ typedef struct nq_step_io {
  * RoPE -> K/V page append at pos -> split-K paged attention over [0, pos] ->
  * O GEMV + residual -> RMSNorm -> gate/up GEMV + SwiGLU -> down GEMV +
  * residual; final RMSNorm -> LM-head GEMV -> argmax (lowest index on ties)
- * -> tokens, pos += 1.
+ * -> tokens, pos += 1. That is 6 kernels per layer (attention is a split
+ * kernel and a combine kernel) plus 2 (LM head, argmax); the gather runs in
+ * layer 0's QKV kernel.
  * Errors: NQ_ERR_STATE if the model is not fully bound; NQ_ERR_INVALID_ARG for
  * bad io; NQ_ERR_HIP on launch failure.
  */

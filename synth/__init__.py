@@ -195,3 +195,16 @@ def decode_page_tables(batch: int, max_pages: int, seed: int = 3, spare_pages: i
     perm = page_permutation(total, seed)
     pt = perm[: batch * max_pages].reshape(batch, max_pages).astype(np.int32)
     return pt, total
+
+
+def fill_device_normal(t, seed: int) -> None:
+    """Fills a device float16 tensor in place with N(0, 1) values from torch's
+    seeded device generator (stand-in contents for a pre-filled KV cache)."""
+    import torch
+    g = torch.Generator(device=t.device)
+    g.manual_seed(int(seed))
+    flat = t.view(-1)
+    step = 1 << 28
+    for i in range(0, flat.numel(), step):
+        blk = flat[i:i + step]
+        blk.copy_(torch.randn(blk.numel(), generator=g, device=t.device, dtype=torch.float32))

@@ -146,7 +146,7 @@ def test_graph_replay_equals_eager_bitwise(tiny, tiny_run):
     np.testing.assert_array_equal(g["tokens"], eager["tokens"])
     np.testing.assert_array_equal(g["logits"].view(np.uint32), eager["logits"].view(np.uint32))
     np.testing.assert_array_equal(g["layer_out"].view(np.uint16), eager["layer_out"].view(np.uint16))
-    assert g["kernels"] == 1 + 6 * SHAPE.layers + 2
+    assert g["kernels"] == 6 * SHAPE.layers + 2
 
 
 def test_batched_ragged_equals_single_sequences(tiny):

@@ -65,7 +65,12 @@ struct GemvArgs {
   void* y = nullptr;                // output
   void* y2 = nullptr;               // optional copy of the residual output (layer_out)
   int epi = 0;
-  // argmax partials (LM head in the step): float [B][T] values, int [B][T] indices
+  // embedding gather folded into the prologue (layer 0 of the step)
+  const void* embed = nullptr;
+  const int32_t* tokens_in = nullptr;
+  int32_t vocab = 0;
+  void* h_out = nullptr;
+  // LM head: per-workgroup greedy (max, index) partials [B][grid]
   float* amax_val = nullptr;
   int32_t* amax_idx = nullptr;
   // QKV epilogue
@@ -79,6 +84,7 @@ struct GemvArgs {
   int32_t* err = nullptr;
 };
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s);
+int gemv_grid_size(int32_t N, int32_t K, int32_t batch);
 
 struct AttnArgs {
   const void* q = nullptr;          // fp16 [B][nh][d]
@@ -103,12 +109,8 @@ hipError_t launch_kv_append(void* k_pool, void* v_pool, int32_t batch, int32_t n
                             int32_t num_pages, const int32_t* pos, const void* k, const void* v,
                             int32_t* err, hipStream_t s);
 
-hipError_t launch_embed(const void* embed, int32_t vocab, int32_t hidden, const int32_t* tokens,
-                        int32_t batch, void* h, int32_t* err, hipStream_t s);
-
-hipError_t launch_argmax_finalize(const float* vals, const int32_t* idx, int32_t tiles,
-                                  int32_t batch, int32_t vocab, int32_t* tokens, int32_t* pos,
-                                  int32_t* hist, int32_t hist_len, int32_t* err, hipStream_t s);
+hipError_t launch_argmax_finalize(const float* vals, const int32_t* idx, int32_t partials, int32_t batch,
+                                  int32_t* tokens, int32_t* pos, int32_t* hist, int32_t hist_len, hipStream_t s);
 
 hipError_t launch_unpack_dev(const void* packed, int32_t N, int32_t K, int32_t kind,
                              int32_t head_dim, int8_t* q_out, uint16_t* s_out, hipStream_t s);

@@ -2,11 +2,12 @@
 //
 // * W4A16 GEMV (fused Q/K/V/O and gate/up/down projections and the LM head;
 //   "How to build your own LLM runtime from scratch", section "What it actually
-//   builds"): packed INT4 tiles streamed with one 1 KiB coalesced load per wave
-//   and group, nibbles turned into exact fp16 codes in registers, v_dot2_f32_f16
-//   against fp16 activations staged in LDS, fp32 accumulation, the group scale
-//   applied to the fp32 partial sum, and fused epilogues (bias + RoPE + KV-page
-//   append, residual add, SwiGLU, fp32 logits + argmax partials).
+//   builds"): packed INT4 tiles streamed with one 1 KiB coalesced buffer load
+//   per wave and group, nibbles turned into exact fp16 codes in registers, the
+//   multiply-accumulate on the matrix cores (v_mfma_f32_16x16x32_f16, the
+//   batch in the MFMA columns) against fp16 activations staged in LDS, the
+//   group scale applied to the fp32 partial sums, and fused epilogues (bias +
+//   RoPE + KV-page append, residual add, SwiGLU, fp32 logits + argmax partials).
 // * Split-K paged decode attention ("What it actually builds": 16-token pages;
 //   daily.dev FAQ on the barrier inside a warp-id branch): each wave stages its
 //   own K/V pages in its own LDS slice and synchronises only itself; the single
@@ -41,9 +42,10 @@ __device__ __forceinline__ void wave_sync() {
 // codes: (q[k], q[k+1]), (q[k+2], q[k+3]), (q[k+4], q[k+5]), (q[k+6], q[k+7]).
 // A nibble n in bits 0-3 of a 16-bit half, OR'ed with 0x6400, is the half
 // 1024 + n; subtracting 1032 leaves q = n - 8 exactly. A nibble in bits 4-7
-// gives 1024 + 16n; (1024 + 16n) / 16 - 72 = n - 8, also exact.
-__device__ __forceinline__ void unpack8(uint32_t w, h2 (&o)[4]) {
-  const uint32_t magic = 0x64006400u;
+// gives 1024 + 16n; (1024 + 16n) / 16 - 72 = n - 8, also exact. ``magic``
+// (0x64006400) is passed in a register so that each mask-and-insert is a
+// single v_and_or_b32 (gfx9 VOP3 cannot take two literal constants).
+__device__ __forceinline__ void unpack8(uint32_t w, uint32_t magic, h2 (&o)[4]) {
   const h2 off_lo = {static_cast<half_t>(-1032.0f), static_cast<half_t>(-1032.0f)};
   const h2 sixteenth = {static_cast<half_t>(0.0625f), static_cast<half_t>(0.0625f)};
   const h2 off_hi = {static_cast<half_t>(-72.0f), static_cast<half_t>(-72.0f)};
@@ -54,23 +56,57 @@ __device__ __forceinline__ void unpack8(uint32_t w, h2 (&o)[4]) {
   o[3] = __builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | magic), sixteenth, off_hi);
 }
 
+__device__ __forceinline__ void unpack8(uint32_t w, h2 (&o)[4]) { unpack8(w, 0x64006400u, o); }
+
 __device__ __forceinline__ float dot2(h2 a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(a, as_h2(b), c, false);
 }
 
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // ============================================================== GEMV
+//
+// Work split: the T = N/16 row tiles of the packed matrix are cut into
+// (tile, K-slice) pieces; a workgroup holds tpw tiles x ks K-slices, one wave
+// each. A wave walks the 1 KiB (tile, group) blocks of its slice, groups
+// g = slice + ks*i, keeping kDepth buffer loads in flight (a ring refilled as
+// each block is consumed). Each block is 16 rows x 128 K: lane l holds row
+// l%16 and K range 32*(l/16)..+31, i.e. one 16x16x32 MFMA A-fragment per
+// 32-bit word. The activations sit in LDS as the MFMA B operand (column =
+// batch row, zero beyond the batch). Per group the four MFMA partial sums of a
+// row are scaled by that row's fp16 group scale in fp32. Slices of a tile are
+// summed through LDS, then the fused epilogue runs on (tile, batch, row) items.
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kDepth = 8;                   // 1 KiB weight loads in flight per wave
+constexpr int kDmaBatch = 8;                // activation copies issued back to back per wave
+constexpr int kBufferFlags = 0x00020000;    // gfx9 raw buffer descriptor word 3
+constexpr size_t kLdsX = 56 * 1024;         // LDS budget for staged activations and gain
 
 struct GemvParams {
-  const uint4* codes;
-  const half_t* scales;
-  int N, K, kind, head_dim, G, T, tpw, ks, ch;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int N, K, kind, head_dim, G, T, tpw, ks, ch, xrow;
   const half_t* x;
   const half_t* gain;
   float eps;
   const half_t* bias;
   void* y;
   half_t* y2;
-  int epi;
+  // embedding gather folded into the prologue: x row b = embed[tokens[b]], and
+  // workgroup 0 also stores it to h_out (the residual stream)
+  const half_t* embed;
+  const int32_t* tokens_in;
+  int vocab;
+  half_t* h_out;
+  // LM head: per-workgroup greedy (max, index) partials [B][gridDim.x]
   float* amax_val;
   int32_t* amax_idx;
   const int32_t* pos;
@@ -83,259 +119,423 @@ struct GemvParams {
   int32_t* err;
 };
 
-constexpr int kUnroll = 8;
-
-template <int B>
-__device__ __forceinline__ void gemv_group(const uint4& wv, half_t s, const half_t* xs, int xstride,
-                                           int gl, int kq, float (&acc)[B]) {
-  h2 q[4][4];
-  unpack8(wv.x, q[0]);
-  unpack8(wv.y, q[1]);
-  unpack8(wv.z, q[2]);
-  unpack8(wv.w, q[3]);
-  const float sf = static_cast<float>(s);
+// Four 16x16x32 MFMAs over one (tile, group) block: d[i] = sum over the
+// group's 128 K of q[row 4*(l/16)+i][k] * x[col l%16][k] (unscaled).
+__device__ __forceinline__ f4 gemv_block_mfma(const u32x4& w, const half_t* xg, uint32_t magic) {
+  f4 d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int b = 0; b < B; ++b) {
-    const uint4* xv = reinterpret_cast<const uint4*>(xs + b * xstride + gl * 128 + kq * 32);
-    float p = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint4 xx = xv[j];
-      p = dot2(q[j][0], xx.x, p);
-      p = dot2(q[j][1], xx.y, p);
-      p = dot2(q[j][2], xx.z, p);
-      p = dot2(q[j][3], xx.w, p);
-    }
-    acc[b] = fmaf(p, sf, acc[b]);
+  for (int j = 0; j < 4; ++j) {
+    h2 q[4];
+    unpack8(w[j], magic, q);
+    const u32x4 qa = {__builtin_bit_cast(uint32_t, q[0]), __builtin_bit_cast(uint32_t, q[1]),
+                      __builtin_bit_cast(uint32_t, q[2]), __builtin_bit_cast(uint32_t, q[3])};
+    const u32x4 xb = *reinterpret_cast<const u32x4*>(xg + j * 8);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, qa), __builtin_bit_cast(half8, xb), d,
+                                               0, 0, 0);
   }
+  return d;
 }
 
-template <int B>
+// acc[i] += d[i] * scale of row 4*(l/16)+i (fp16 scales of four rows in sc)
+__device__ __forceinline__ void scale_acc(f4& acc, const f4& d, const u32x2& sc) {
+  const h2 s01 = as_h2(sc.x), s23 = as_h2(sc.y);
+  acc[0] = fmaf(d[0], static_cast<float>(s01[0]), acc[0]);
+  acc[1] = fmaf(d[1], static_cast<float>(s01[1]), acc[1]);
+  acc[2] = fmaf(d[2], static_cast<float>(s23[0]), acc[2]);
+  acc[3] = fmaf(d[3], static_cast<float>(s23[1]), acc[3]);
+}
+
+// Greedy tie rule: larger value wins, equal values go to the lower index.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
+// s_waitcnt immediates (gfx9 encoding): wait for LDS/scalar memory only, or
+// for LDS/scalar memory and until at most n vector-memory operations are
+// outstanding.
+constexpr int kWaitLgkm0 = 0xC07F;
+constexpr int wait_vm_lgkm0(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
+
+template <int B, int EPI, bool GAIN>
 __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nw = blockDim.x >> 6;
-  const int r = lane & 15, kq = lane >> 4;
+  const int col = lane & 15, kb = lane >> 4;
   const int tl = wave / p.ks, ksi = wave % p.ks;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * p.tpw + tl;
+  const int t = static_cast<int>(blockIdx.x) * p.tpw + tl;
   const bool tile_ok = t < p.T;  // wave-uniform
-  const int xstride = p.ch * 128;
+  const int xrow = p.xrow;       // halfs per staged row, a multiple of 512 (1 KiB)
+  // LDS: [B] activation rows | gain row (GAIN) | zero block | red | ssq | lg
   half_t* xs = reinterpret_cast<half_t*>(smem);
-  float* red = reinterpret_cast<float*>(smem + static_cast<size_t>(B) * xstride * 2);
-  float* rs = red + nw * B * 16;
-  float* lg = rs + B;  // [tpw][B][16] logits for the argmax partials
+  half_t* gs = xs + B * xrow;
+  half_t* zero = gs + (GAIN ? xrow : 0);
+  float* red = reinterpret_cast<float*>(zero + 128);  // [nw][B][16]
+  float* ssq = red + nw * B * 16;                      // [nw][B]
+  float* lg = ssq + nw * B;                            // [tpw][B][16]
+  const uint32_t magic = opaque(0x64006400u);
+  const int items = p.tpw * B * 16;
 
-  if (p.gain) {
-    float ss[B];
+  // Inputs of the fused QKV epilogue (bias, position, RoPE cos/sin, page id)
+  // do not depend on the GEMV: fetch them now, their latency hides under the
+  // weight stream.
+  float e_bias = 0.0f, e_pbias = 0.0f, e_cos = 1.0f, e_sin = 0.0f;
+  int e_pos = 0, e_page = -1;
+  if constexpr (EPI == EPI_QKV_ROPE_KV) {
+    if (tid < items) {
+      const int tl2 = tid / (B * 16), b = (tid / 16) % B, rr = tid & 15;
+      const int64_t tt = static_cast<int64_t>(blockIdx.x) * p.tpw + tl2;
+      if (tt < p.T) {
+        const int64_t n = tile_row_logical(p.kind, p.N, p.head_dim, tt, rr);
+        const int64_t np = tile_row_logical(p.kind, p.N, p.head_dim, tt, rr ^ 8);
+        e_bias = static_cast<float>(p.bias[n]);
+        e_pbias = static_cast<float>(p.bias[np]);
+        e_pos = p.pos[b];
+        const int half = p.head_dim / 2;
+        if (e_pos >= 0 && e_pos < p.max_pos) {
+          const int j = static_cast<int>(n % p.head_dim) % half;
+          const float2 cs = *reinterpret_cast<const float2*>(p.rope + (static_cast<int64_t>(e_pos) * half + j) * 2);
+          e_cos = cs.x;
+          e_sin = cs.y;
+        }
+        const int pg = e_pos / kPageTokens;
+        if (e_pos >= 0 && pg < p.max_pages) e_page = p.pt[static_cast<int64_t>(b) * p.max_pages + pg];
+      }
+    }
+  }
+
+  // Buffer descriptors over this tile's codes and scales: the per-group offset
+  // is a scalar, the per-lane offset a constant; reads past the tile give 0.
+  const int tq = tile_ok ? t : 0;
+  const int wbytes = tile_ok ? p.G * kBlockBytes : 0, sbytes = tile_ok ? p.G * 32 : 0;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.codes) + static_cast<size_t>(tq) * p.G * kBlockBytes, 0, wbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.scales) + static_cast<size_t>(tq) * p.G * 32, 0, sbytes, kBufferFlags);
+  const int wvoff = lane * 16, svoff = kb * 8;
+  // B fragment of this lane: its batch row, or the zero block for columns >= B
+  const half_t* xlane = (col < B ? xs + col * xrow : zero) + kb * 32;
+  const int xstep = col < B ? 128 : 0;
+  if (tid < 16) reinterpret_cast<uint4*>(zero)[tid] = make_uint4(0u, 0u, 0u, 0u);
+
+  // input token ids (embedding gather in the prologue): lane b holds row b's
+  int tok_lane = 0;
+  if (p.embed) {
+    tok_lane = lane < B ? p.tokens_in[lane] : 0;
+    if (lane < B && (tok_lane < 0 || tok_lane >= p.vocab) && blockIdx.x == 0 && wave == 0) raise_flag(p.err, 4);
+  }
+
+  u32x4 wv[kDepth];
+  u32x2 sv[kDepth];
+  f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float ss[B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) ss[b] = 0.0f;
-    for (int i = tid; i < p.K / 8; i += blockDim.x) {
+  for (int b = 0; b < B; ++b) ss[b] = 0.0f;
+
+  for (int c0 = 0; c0 < p.G; c0 += p.ch) {
+    const int c1 = min(p.G, c0 + p.ch);
+    const int n_c = (c1 - c0 - ksi + p.ks - 1) / p.ks;  // this wave's groups in the chunk (may be <= 0)
+    const int n8 = (c1 - c0) * 16;                      // 16-byte items per staged row
+    const int rblk = (n8 + 63) / 64;                    // 1 KiB blocks per staged row
+    if (c0 > 0) __syncthreads();                        // the previous chunk is consumed
+    // (1) Activations (and gain) straight into LDS, one 1 KiB block per wave
+    //     instruction, issued before the weights: the memory counter retires
+    //     in order, so they can be waited for without waiting for the weights.
+    const int nblk = (B + (GAIN ? 1 : 0)) * rblk;
+    const int mine = (nblk - wave + nw - 1) / nw;  // blocks of this wave
+    for (int r0 = 0; r0 < mine; r0 += kDmaBatch) {
+      // straight-line batches: the copies go out back to back
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const uint4 v = *reinterpret_cast<const uint4*>(p.x + static_cast<int64_t>(b) * p.K + i * 8);
-        const half_t* hv = reinterpret_cast<const half_t*>(&v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float f = static_cast<float>(hv[e]);
-          ss[b] = fmaf(f, f, ss[b]);
+      for (int q = 0; q < kDmaBatch; ++q) {
+        const int bi = wave + (r0 + q) * nw;
+        if (r0 + q < mine) {
+          const int r = bi / rblk, j = bi - r * rblk;
+          const int item = j * 64 + lane;
+          const half_t* src;
+          half_t* dst;
+          if (r < B) {
+            const half_t* xr = p.x + static_cast<int64_t>(r) * p.K;
+            if (p.embed) {  // activation row r is the embedding row of the input token
+              int tok = __builtin_amdgcn_readlane(tok_lane, r);
+              if (tok < 0 || tok >= p.vocab) tok = 0;
+              xr = p.embed + static_cast<int64_t>(tok) * p.K;
+            }
+            src = xr + static_cast<int64_t>(c0) * 128 + item * 8;
+            dst = xs + r * xrow + j * 512;
+          } else {
+            src = p.gain + static_cast<int64_t>(c0) * 128 + item * 8;
+            dst = gs + j * 512;
+          }
+          if (item < n8) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // (2) The weight ring: exactly 2 * kDepth loads per wave (absent groups
+    //     read past the tile and return 0), so the wait below is exact.
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      const bool ok = u < n_c;
+      const int g = c0 + ksi + p.ks * u;
+      wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff, ok ? g * kBlockBytes : wbytes, 0);
+      sv[u] = __builtin_amdgcn_raw_buffer_load_b64(srs, svoff, ok ? g * 32 : sbytes, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * kDepth));  // this wave's LDS writes have landed
+    __builtin_amdgcn_s_barrier();                     // ... and every wave's
+    __builtin_amdgcn_sched_barrier(0);
+    // (3) x * gain in place, sum(x^2) (1/rms multiplies the outputs later);
+    //     workgroup 0 also stores the gathered embedding rows as the residual
+    if constexpr (GAIN) {
+      for (int i = tid; i < B * n8; i += blockDim.x) {
+        const int b = i / n8, j = i - b * n8;
+        uint4 v = *reinterpret_cast<const uint4*>(xs + b * xrow + j * 8);
+        const uint4 gv = *reinterpret_cast<const uint4*>(gs + j * 8);
+        if (p.h_out && blockIdx.x == 0)
+          *reinterpret_cast<uint4*>(p.h_out + static_cast<int64_t>(b) * p.K + static_cast<int64_t>(c0) * 128 + j * 8) = v;
+        half_t* hv = reinterpret_cast<half_t*>(&v);
+        const half_t* gh = reinterpret_cast<const half_t*>(&gv);
+        float sacc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = static_cast<float>(hv[e]);
+          sacc = fmaf(f, f, sacc);
+          hv[e] = static_cast<half_t>(f * static_cast<float>(gh[e]));
+        }
+#pragma unroll
+        for (int bb = 0; bb < B; ++bb)
+          if (bb == b) ss[bb] += sacc;
+        *reinterpret_cast<uint4*>(xs + b * xrow + j * 8) = v;
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // (4) the scale of group i is applied while group i+1 is on the matrix cores
+    for (int ib = 0; ib < n_c; ib += kDepth) {
+      f4 dprev;
+      u32x2 sprev;
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const int i = ib + u;
+        if (i < n_c) {
+          const f4 d = gemv_block_mfma(wv[u], xlane + (ksi + p.ks * i) * xstep, magic);
+          if (u > 0) scale_acc(acc, dprev, sprev);
+          dprev = d;
+          sprev = sv[u];
+          if (i + kDepth < n_c) {  // refill the slot just consumed
+            const int gn = c0 + ksi + p.ks * (i + kDepth);
+            wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff, gn * kBlockBytes, 0);
+            sv[u] = __builtin_amdgcn_raw_buffer_load_b64(srs, svoff, gn * 32, 0);
+          }
+        }
+      }
+      scale_acc(acc, dprev, sprev);
+    }
+  }
+
+  // per-wave partial sums of x^2, and the tile rows of this wave
+  if constexpr (GAIN) {
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       float v = ss[b];
       for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-      if (lane == 0) red[wave * B + b] = v;
-    }
-    __syncthreads();
-    if (tid < B) {
-      float v = 0.0f;
-      for (int w = 0; w < nw; ++w) v += red[w * B + tid];
-      rs[tid] = 1.0f / sqrtf(v / static_cast<float>(p.K) + p.eps);
+      if (lane == 0) ssq[wave * B + b] = v;
     }
   }
-
-  float acc[B];
+  __syncthreads();  // every wave is done reading xs; red is free
+  if (col < B) {
 #pragma unroll
-  for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-
-  for (int c0 = 0; c0 < p.G; c0 += p.ch) {
-    const int c1 = min(p.G, c0 + p.ch);
-    const int n8 = (c1 - c0) * 16;  // 16-byte items per batch row in this chunk
-    __syncthreads();
-    for (int i = tid; i < B * n8; i += blockDim.x) {
-      const int b = i / n8, j = i - b * n8;
-      const int64_t k = static_cast<int64_t>(c0) * 128 + j * 8;
-      uint4 v = *reinterpret_cast<const uint4*>(p.x + static_cast<int64_t>(b) * p.K + k);
-      if (p.gain) {
-        const uint4 gv = *reinterpret_cast<const uint4*>(p.gain + k);
-        half_t* hv = reinterpret_cast<half_t*>(&v);
-        const half_t* gh = reinterpret_cast<const half_t*>(&gv);
-        const float sc = rs[b];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          hv[e] = static_cast<half_t>(static_cast<float>(hv[e]) * sc * static_cast<float>(gh[e]));
-      }
-      *reinterpret_cast<uint4*>(xs + b * xstride + j * 8) = v;
-    }
-    __syncthreads();
-    if (tile_ok) {
-      const uint4* wp = p.codes + static_cast<size_t>(t) * p.G * 64 + lane;
-      const half_t* sp = p.scales + static_cast<size_t>(t) * p.G * 16 + r;
-      int g = c0 + ksi;
-      for (; g + (kUnroll - 1) * p.ks < c1; g += kUnroll * p.ks) {
-        uint4 wv[kUnroll];
-        half_t sv[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          wv[u] = wp[static_cast<size_t>(g + u * p.ks) * 64];
-          sv[u] = sp[static_cast<size_t>(g + u * p.ks) * 16];
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) gemv_group<B>(wv[u], sv[u], xs, xstride, g + u * p.ks - c0, kq, acc);
-      }
-      for (; g < c1; g += p.ks) {
-        const uint4 wv = wp[static_cast<size_t>(g) * 64];
-        const half_t sv = sp[static_cast<size_t>(g) * 16];
-        gemv_group<B>(wv, sv, xs, xstride, g - c0, kq, acc);
-      }
-    }
-  }
-
-  // sum the four K quarters of each row, then hand the wave's rows to LDS
-#pragma unroll
-  for (int b = 0; b < B; ++b) {
-    acc[b] += __shfl_xor(acc[b], 16);
-    acc[b] += __shfl_xor(acc[b], 32);
-  }
-  __syncthreads();  // xs and red may be reused below
-  if (lane < 16) {
-#pragma unroll
-    for (int b = 0; b < B; ++b) red[(wave * B + b) * 16 + r] = acc[b];
+    for (int i = 0; i < 4; ++i) red[(wave * B + col) * 16 + 4 * kb + i] = acc[i];
   }
   __syncthreads();
 
-  const int items = p.tpw * B * 16;
   for (int i = tid; i < items; i += blockDim.x) {
     const int tl2 = i / (B * 16), b = (i / 16) % B, rr = i & 15;
     const int64_t tt = static_cast<int64_t>(blockIdx.x) * p.tpw + tl2;
     if (tt >= p.T) continue;
+    float rsb = 1.0f;
+    if constexpr (GAIN) {
+      float v = 0.0f;
+      for (int w = 0; w < nw; ++w) v += ssq[w * B + b];
+      rsb = 1.0f / sqrtf(v / static_cast<float>(p.K) + p.eps);
+    }
     float yv = 0.0f, yp = 0.0f;
     for (int k2 = 0; k2 < p.ks; ++k2) {
       yv += red[((tl2 * p.ks + k2) * B + b) * 16 + rr];
       yp += red[((tl2 * p.ks + k2) * B + b) * 16 + (rr ^ 8)];
     }
+    yv *= rsb;
+    yp *= rsb;
     const int64_t n = tile_row_logical(p.kind, p.N, p.head_dim, tt, rr);
     const int64_t N = p.N;
-    switch (p.epi) {
-      case NQ_EPI_STORE_F16:
-        if (n < N) static_cast<half_t*>(p.y)[b * N + n] = static_cast<half_t>(yv);
-        break;
-      case NQ_EPI_BIAS_F16:
-        if (n < N) static_cast<half_t*>(p.y)[b * N + n] = static_cast<half_t>(yv + static_cast<float>(p.bias[n]));
-        break;
-      case NQ_EPI_RESIDUAL_F16:
-        if (n < N) {
-          half_t* yo = static_cast<half_t*>(p.y) + b * N + n;
-          const half_t v = static_cast<half_t>(static_cast<float>(*yo) + yv);
-          *yo = v;
-          if (p.y2) p.y2[b * N + n] = v;
+    if constexpr (EPI == NQ_EPI_STORE_F16) {
+      if (n < N) static_cast<half_t*>(p.y)[b * N + n] = static_cast<half_t>(yv);
+    } else if constexpr (EPI == NQ_EPI_BIAS_F16) {
+      if (n < N) static_cast<half_t*>(p.y)[b * N + n] = static_cast<half_t>(yv + static_cast<float>(p.bias[n]));
+    } else if constexpr (EPI == NQ_EPI_RESIDUAL_F16) {
+      if (n < N) {
+        half_t* yo = static_cast<half_t*>(p.y) + b * N + n;
+        const half_t v = static_cast<half_t>(static_cast<float>(*yo) + yv);
+        *yo = v;
+        if (p.y2) p.y2[b * N + n] = v;
+      }
+    } else if constexpr (EPI == NQ_EPI_SWIGLU_F16) {
+      if (rr < 8) {
+        const int64_t I = N / 2;
+        const float a = yv / (1.0f + expf(-yv)) * yp;
+        static_cast<half_t*>(p.y)[b * I + 8 * tt + rr] = static_cast<half_t>(a);
+      }
+    } else if constexpr (EPI == NQ_EPI_STORE_F32) {
+      if (n < N && p.y) static_cast<float*>(p.y)[b * N + n] = yv;
+      lg[(tl2 * B + b) * 16 + rr] = (n < N) ? yv : -INFINITY;
+    } else if constexpr (EPI == EPI_QKV_ROPE_KV) {
+      // prefetched values belong to item tid; further items (if any) load theirs here
+      float bn = e_bias, bp = e_pbias, cs = e_cos, sn = e_sin;
+      int ps = e_pos, page = e_page;
+      const int d = p.head_dim, half = d / 2;
+      const int hb = static_cast<int>(n / d), i2 = static_cast<int>(n % d);
+      if (i != tid) {
+        const int64_t np = tile_row_logical(p.kind, p.N, p.head_dim, tt, rr ^ 8);
+        bn = static_cast<float>(p.bias[n]);
+        bp = static_cast<float>(p.bias[np]);
+        ps = p.pos[b];
+        cs = 1.0f;
+        sn = 0.0f;
+        if (ps >= 0 && ps < p.max_pos) {
+          cs = p.rope[(static_cast<int64_t>(ps) * half + i2 % half) * 2];
+          sn = p.rope[(static_cast<int64_t>(ps) * half + i2 % half) * 2 + 1];
         }
-        break;
-      case NQ_EPI_SWIGLU_F16:
-        if (rr < 8) {
-          const int64_t I = N / 2;
-          const float a = yv / (1.0f + expf(-yv)) * yp;
-          static_cast<half_t*>(p.y)[b * I + 8 * tt + rr] = static_cast<half_t>(a);
-        }
-        break;
-      case NQ_EPI_STORE_F32:
-        if (n < N && p.y) static_cast<float*>(p.y)[b * N + n] = yv;
-        lg[(tl2 * B + b) * 16 + rr] = (n < N) ? yv : -INFINITY;
-        break;
-      case EPI_QKV_ROPE_KV: {
-        const int d = p.head_dim, half = d / 2;
-        const int hb = static_cast<int>(n / d), i2 = static_cast<int>(n % d);
-        const half_t v16 = static_cast<half_t>(yv + static_cast<float>(p.bias[n]));
-        const int ps = p.pos[b];
-        half_t outv = v16;
-        if (hb < p.n_heads + p.n_kv) {
-          const int64_t np = tile_row_logical(p.kind, p.N, p.head_dim, tt, rr ^ 8);
-          const half_t p16 = static_cast<half_t>(yp + static_cast<float>(p.bias[np]));
-          if (ps < 0 || ps >= p.max_pos) {
-            raise_flag(p.err, 1);
-            break;
-          }
-          const int j = i2 % half;
-          const float c = p.rope[(static_cast<int64_t>(ps) * half + j) * 2];
-          const float sn = p.rope[(static_cast<int64_t>(ps) * half + j) * 2 + 1];
-          const float xi = static_cast<float>(v16), xp = static_cast<float>(p16);
-          outv = static_cast<half_t>(i2 < half ? xi * c - xp * sn : xi * c + xp * sn);
-        }
-        if (hb < p.n_heads) {
-          static_cast<half_t*>(p.y)[(static_cast<int64_t>(b) * p.n_heads + hb) * d + i2] = outv;
+        const int pg = ps / kPageTokens;
+        page = (ps >= 0 && pg < p.max_pages) ? p.pt[static_cast<int64_t>(b) * p.max_pages + pg] : -1;
+      }
+      const half_t v16 = static_cast<half_t>(yv + bn);
+      half_t outv = v16;
+      bool ok = true;
+      if (hb < p.n_heads + p.n_kv) {
+        const half_t p16 = static_cast<half_t>(yp + bp);
+        if (ps < 0 || ps >= p.max_pos) {
+          raise_flag(p.err, 1);
+          ok = false;
         } else {
-          const bool is_k = hb < p.n_heads + p.n_kv;
-          const int kvh = is_k ? hb - p.n_heads : hb - p.n_heads - p.n_kv;
-          const int pg = ps / kPageTokens;
-          if (ps < 0 || pg >= p.max_pages) {
-            raise_flag(p.err, 1);
-            break;
-          }
-          const int page = p.pt[static_cast<int64_t>(b) * p.max_pages + pg];
-          if (page < 0 || page >= p.num_pages) {
-            raise_flag(p.err, 1);
-            break;
-          }
+          const float xi = static_cast<float>(v16), xp = static_cast<float>(p16);
+          outv = static_cast<half_t>(i2 < half ? xi * cs - xp * sn : xi * cs + xp * sn);
+        }
+      }
+      if (ok && hb < p.n_heads) {
+        static_cast<half_t*>(p.y)[(static_cast<int64_t>(b) * p.n_heads + hb) * d + i2] = outv;
+      } else if (ok) {
+        const bool is_k = hb < p.n_heads + p.n_kv;
+        const int kvh = is_k ? hb - p.n_heads : hb - p.n_heads - p.n_kv;
+        if (page < 0 || page >= p.num_pages) {
+          raise_flag(p.err, 1);
+        } else {
           half_t* base = is_k ? p.kv_k : p.kv_v;
           base[((static_cast<int64_t>(page) * p.n_kv + kvh) * kPageTokens + ps % kPageTokens) * d + i2] = outv;
         }
-        break;
       }
-      default:
-        break;
     }
   }
 
-  if (p.epi == NQ_EPI_STORE_F32 && p.amax_val) {
-    __syncthreads();
-    if (tid < p.tpw * B) {
-      const int tl2 = tid / B, b = tid % B;
-      const int64_t tt = static_cast<int64_t>(blockIdx.x) * p.tpw + tl2;
-      if (tt < p.T) {
+  if constexpr (EPI == NQ_EPI_STORE_F32) {
+    if (p.amax_val) {
+      __syncthreads();
+      // this workgroup's best (value, index) per batch row
+      if (tid < B) {
+        const int b = tid;
         float best = -INFINITY;
         int bi = 0x7fffffff;
         bool nan = false;
-        for (int rr = 0; rr < 16; ++rr) {
-          const float v = lg[(tl2 * B + b) * 16 + rr];
-          const int n = static_cast<int>(tile_row_logical(p.kind, p.N, p.head_dim, tt, rr));
-          if (v != v) { nan = true; continue; }
-          if (n < p.N && (v > best || (v == best && n < bi))) { best = v; bi = n; }
+        for (int tl2 = 0; tl2 < p.tpw; ++tl2) {
+          const int64_t tt = static_cast<int64_t>(blockIdx.x) * p.tpw + tl2;
+          if (tt >= p.T) break;
+          for (int rr = 0; rr < 16; ++rr) {
+            const float v = lg[(tl2 * B + b) * 16 + rr];
+            const int n = static_cast<int>(tile_row_logical(p.kind, p.N, p.head_dim, tt, rr));
+            if (v != v) {
+              nan = true;
+              continue;
+            }
+            if (n < p.N && better(v, n, best, bi)) {
+              best = v;
+              bi = n;
+            }
+          }
         }
         if (nan) raise_flag(p.err, 8);
-        p.amax_val[static_cast<int64_t>(b) * p.T + tt] = best;
-        p.amax_idx[static_cast<int64_t>(b) * p.T + tt] = bi;
+        p.amax_val[static_cast<int64_t>(b) * gridDim.x + blockIdx.x] = best;
+        p.amax_idx[static_cast<int64_t>(b) * gridDim.x + blockIdx.x] = bi;
       }
     }
   }
 }
 
 struct GemvShape {
-  int tpw, ks, ch, threads;
+  int tpw, ks, ch, xrow, threads;
   size_t lds;
 };
 
-static GemvShape gemv_shape(int T, int G, int B) {
+// Each wave owns at most kDepth groups of a tile where possible, so that all
+// of its weight loads are in flight at once; small-N matrices are split
+// further along K (at least 4 groups per slice) so that about 2048 waves share
+// the work; a workgroup has at least 4 waves. The staged activations (plus the
+// gain) get at most kLdsX bytes; longer K is processed in chunks.
+static GemvShape gemv_shape(int T, int G, int B, bool gain) {
   GemvShape s;
-  s.ks = std::min(16, std::max(1, (G + 6) / 7));
-  s.tpw = 1;
-  while (s.tpw * 2 * s.ks <= 16 && T / (s.tpw * 2) >= 1024) s.tpw *= 2;
-  s.ch = std::min(G, std::max(1, (48 * 1024) / (B * 256)));
+  const int need = (G + kDepth - 1) / kDepth;
+  const int spread = std::min((2048 + T - 1) / T, std::max(1, G / 4));
+  s.ks = std::max(1, std::min(16, std::max(need, spread)));
+  s.tpw = std::max(1, std::min(16 / s.ks, 4 / s.ks > 0 ? 4 / s.ks : 1));
+  const int rows = B + (gain ? 1 : 0);
+  const int fit = static_cast<int>(kLdsX / (static_cast<size_t>(rows) * 256)) / 4 * 4;  // whole 1 KiB blocks
+  s.ch = G <= fit ? G : std::max(s.ks, fit / s.ks * s.ks);
+  s.xrow = (s.ch * 128 + 511) / 512 * 512;
   s.threads = s.tpw * s.ks * 64;
   const int nw = s.tpw * s.ks;
-  s.lds = static_cast<size_t>(B) * s.ch * 256 + static_cast<size_t>(nw) * B * 16 * 4 + B * 4 +
+  s.lds = static_cast<size_t>(rows) * s.xrow * 2 + 256 + static_cast<size_t>(nw) * B * 16 * 4 + nw * B * 4 +
           static_cast<size_t>(s.tpw) * B * 16 * 4;
   return s;
+}
+
+int gemv_grid_size(int32_t N, int32_t K, int32_t batch) {
+  const int T = static_cast<int>(tiles_of(N));
+  const GemvShape sh = gemv_shape(T, K / kGroup, batch, true);
+  return (T + sh.tpw - 1) / sh.tpw;
+}
+
+template <int B, bool GAIN>
+static hipError_t launch_gemv_e(int epi, dim3 grid, dim3 block, size_t lds, hipStream_t stream, const GemvParams& p) {
+  switch (epi) {
+    case NQ_EPI_STORE_F16: gemv_w4a16_kernel<B, NQ_EPI_STORE_F16, GAIN><<<grid, block, lds, stream>>>(p); break;
+    case NQ_EPI_BIAS_F16: gemv_w4a16_kernel<B, NQ_EPI_BIAS_F16, GAIN><<<grid, block, lds, stream>>>(p); break;
+    case NQ_EPI_RESIDUAL_F16: gemv_w4a16_kernel<B, NQ_EPI_RESIDUAL_F16, GAIN><<<grid, block, lds, stream>>>(p); break;
+    case NQ_EPI_SWIGLU_F16: gemv_w4a16_kernel<B, NQ_EPI_SWIGLU_F16, GAIN><<<grid, block, lds, stream>>>(p); break;
+    case NQ_EPI_STORE_F32: gemv_w4a16_kernel<B, NQ_EPI_STORE_F32, GAIN><<<grid, block, lds, stream>>>(p); break;
+    case EPI_QKV_ROPE_KV: gemv_w4a16_kernel<B, EPI_QKV_ROPE_KV, GAIN><<<grid, block, lds, stream>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int B>
+static hipError_t launch_gemv_g(bool gain, int epi, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                                const GemvParams& p) {
+  return gain ? launch_gemv_e<B, true>(epi, grid, block, lds, stream, p)
+              : launch_gemv_e<B, false>(epi, grid, block, lds, stream, p);
+}
+
+static hipError_t launch_gemv_b(int batch, bool gain, int epi, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                                const GemvParams& p) {
+  switch (batch) {
+    case 1: return launch_gemv_g<1>(gain, epi, grid, block, lds, stream, p);
+    case 2: return launch_gemv_g<2>(gain, epi, grid, block, lds, stream, p);
+    case 3: return launch_gemv_g<3>(gain, epi, grid, block, lds, stream, p);
+    case 4: return launch_gemv_g<4>(gain, epi, grid, block, lds, stream, p);
+    case 5: return launch_gemv_g<5>(gain, epi, grid, block, lds, stream, p);
+    case 6: return launch_gemv_g<6>(gain, epi, grid, block, lds, stream, p);
+    case 7: return launch_gemv_g<7>(gain, epi, grid, block, lds, stream, p);
+    case 8: return launch_gemv_g<8>(gain, epi, grid, block, lds, stream, p);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
@@ -346,19 +546,23 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
   p.head_dim = a.head_dim;
   p.G = a.K / kGroup;
   p.T = static_cast<int>(tiles_of(a.N));
-  const GemvShape sh = gemv_shape(p.T, p.G, a.batch);
+  const GemvShape sh = gemv_shape(p.T, p.G, a.batch, a.norm_gain != nullptr);
   p.tpw = sh.tpw;
   p.ks = sh.ks;
   p.ch = sh.ch;
-  p.codes = static_cast<const uint4*>(a.packed);
-  p.scales = reinterpret_cast<const half_t*>(static_cast<const uint8_t*>(a.packed) + codes_bytes(a.N, a.K));
+  p.xrow = sh.xrow;
+  p.codes = static_cast<const uint8_t*>(a.packed);
+  p.scales = static_cast<const uint8_t*>(a.packed) + codes_bytes(a.N, a.K);
   p.x = static_cast<const half_t*>(a.x);
   p.gain = static_cast<const half_t*>(a.norm_gain);
   p.eps = a.eps;
   p.bias = static_cast<const half_t*>(a.bias);
   p.y = a.y;
   p.y2 = static_cast<half_t*>(a.y2);
-  p.epi = a.epi;
+  p.embed = static_cast<const half_t*>(a.embed);
+  p.tokens_in = a.tokens_in;
+  p.vocab = a.vocab;
+  p.h_out = static_cast<half_t*>(a.h_out);
   p.amax_val = a.amax_val;
   p.amax_idx = a.amax_idx;
   p.pos = a.pos;
@@ -373,20 +577,23 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
   p.max_pos = a.max_pos;
   p.err = a.err;
   const dim3 grid((p.T + p.tpw - 1) / p.tpw), block(sh.threads);
-  switch (a.batch) {
-#define NQ_CASE(BB) \
-  case BB: gemv_w4a16_kernel<BB><<<grid, block, sh.lds, stream>>>(p); break;
-    NQ_CASE(1) NQ_CASE(2) NQ_CASE(3) NQ_CASE(4) NQ_CASE(5) NQ_CASE(6) NQ_CASE(7) NQ_CASE(8)
-#undef NQ_CASE
-    default:
-      return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return launch_gemv_b(a.batch, a.norm_gain != nullptr, a.epi, grid, block, sh.lds, stream, p);
 }
 
 // ============================================================== attention
+//
+// Split-K paged decode attention. Workgroup (s, kv head, sequence) covers a
+// contiguous page range of the sequence; its kAttnWaves waves take pages
+// w, w+kAttnWaves, ... and each keeps one page in flight ahead of the one it
+// computes. A wave stages its page in its own LDS slice and synchronises only
+// itself; the block barrier sits in uniform control flow after the page loop,
+// and the tail page is masked by position. The query heads of a KV head share
+// every K/V load (GQA). When one workgroup covers the whole context it writes
+// the output; otherwise workgroups write (max, sum, output) partials and the
+// combine kernel merges them with the log-sum-exp rule.
 
-constexpr int kMinPagesPerSplit = 2;
+constexpr int kAttnWaves = 8;
+constexpr int kMinPagesPerSplit = kAttnWaves;
 constexpr int kMaxSplits = 64;
 
 int attn_splits_for(int32_t max_pages) {
@@ -397,12 +604,10 @@ size_t attn_partial_bytes(int32_t batch, int32_t n_heads, int32_t head_dim, int3
   return static_cast<size_t>(batch) * n_heads * splits * (head_dim + 2) * sizeof(float);
 }
 
-__device__ __forceinline__ void split_range(int len, int max_pages, int S, int s, int& p0, int& p1) {
-  int npages = (len + kPageTokens - 1) / kPageTokens;
-  npages = min(npages, max_pages);
-  const int per = max(kMinPagesPerSplit, (npages + S - 1) / S);
-  p0 = s * per;
-  p1 = min(npages, p0 + per);
+__device__ __forceinline__ void split_geometry(int len, int max_pages, int S, int& npages, int& per, int& nact) {
+  npages = min((len + kPageTokens - 1) / kPageTokens, max_pages);
+  per = max(kMinPagesPerSplit, (npages + S - 1) / S);
+  nact = (npages + per - 1) / per;
 }
 
 struct AttnParams {
@@ -420,43 +625,47 @@ struct AttnParams {
   int32_t* err;
 };
 
-// grid (S, n_kv, B), 256 threads = 4 waves. Wave w walks pages p0+w, p0+w+4, ...
 template <int D, int REP>
-__global__ __launch_bounds__(256) void attn_split_kernel(AttnParams a) {
-  constexpr int DC = D / 4;       // dims per lane in the score phase
-  constexpr int DPL = D / 64;     // dims per lane in the PV phase
-  constexpr int PAGE_U4 = 16 * D * 2 / 16;  // uint4 per page
-  constexpr int U4_PER_LANE = PAGE_U4 / 64;
-  __shared__ __align__(16) half_t lk[4][16 * D];
-  __shared__ __align__(16) half_t lv[4][16 * D];
-  __shared__ float lp[4][REP][16];
-  __shared__ float red_m[4][REP], red_l[4][REP];
-  __shared__ float red_o[4][REP][D];
+__global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnParams a) {
+  constexpr int DC = D / 4;                 // dims per lane in the score phase
+  constexpr int DPL = D / 64;               // dims per lane in the PV phase
+  constexpr int U4 = 16 * D * 2 / 16 / 64;  // uint4 per lane per page (K or V)
+  constexpr int NW = kAttnWaves;
+  __shared__ __align__(16) half_t lk[NW][16 * D];
+  __shared__ __align__(16) half_t lv[NW][16 * D];
+  __shared__ float lp[NW][REP][16];
+  __shared__ float red_m[NW][REP], red_l[NW][REP];
+  __shared__ float red_o[NW][REP][D];
 
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int t = lane >> 2, c = lane & 3;
   const int len = a.lens[b] + a.len_add;
-  if (len > a.max_pages * kPageTokens) {
-    if (s == 0 && tid == 0) raise_flag(a.err, 2);
+  int npages, per, nact;
+  split_geometry(len, a.max_pages, a.S, npages, per, nact);
+  if (s == 0 && tid == 0 && len > a.max_pages * kPageTokens) raise_flag(a.err, 2);
+  const int p0 = s * per, p1 = min(npages, p0 + per);
+  if (len <= 0 || p0 >= p1) {
+    if (len <= 0 && s == 0) {  // empty context: zero output
+      for (int i = tid; i < REP * D; i += 64 * NW)
+        a.out[(static_cast<int64_t>(b) * a.n_heads + kvh * REP + i / D) * D + i % D] = static_cast<half_t>(0.0f);
+    }
+    return;  // block-uniform
   }
-  int p0, p1;
-  split_range(len, a.max_pages, a.S, s, p0, p1);
-  if (len <= 0 || p0 >= p1) return;  // block-uniform
 
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   h2 qr[REP][DC / 2];
 #pragma unroll
   for (int h = 0; h < REP; ++h) {
-    const uint4* src = reinterpret_cast<const uint4*>(
+    const u32x4* src = reinterpret_cast<const u32x4*>(
         a.q + (static_cast<int64_t>(b) * a.n_heads + kvh * REP + h) * D + c * DC);
 #pragma unroll
     for (int j = 0; j < DC / 8; ++j) {
-      const uint4 v = src[j];
-      qr[h][4 * j + 0] = as_h2(v.x);
-      qr[h][4 * j + 1] = as_h2(v.y);
-      qr[h][4 * j + 2] = as_h2(v.z);
-      qr[h][4 * j + 3] = as_h2(v.w);
+      const u32x4 v = src[j];
+      qr[h][4 * j + 0] = as_h2(v[0]);
+      qr[h][4 * j + 1] = as_h2(v[1]);
+      qr[h][4 * j + 2] = as_h2(v[2]);
+      qr[h][4 * j + 3] = as_h2(v[3]);
     }
   }
   float m[REP], l[REP], o[REP][DPL];
@@ -468,95 +677,116 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams a) {
     for (int e = 0; e < DPL; ++e) o[h][e] = 0.0f;
   }
 
-  for (int pg = p0 + w; pg < p1; pg += 4) {  // wave-uniform trip count, no block barrier inside
-    const int page = a.pt[static_cast<int64_t>(b) * a.max_pages + pg];
-    const bool page_ok = page >= 0 && page < a.num_pages;
-    if (!page_ok) {
-      if (lane == 0) raise_flag(a.err, 2);
-      continue;
-    }
-    const int valid = min(kPageTokens, len - pg * kPageTokens);
-    const uint4* ksrc = reinterpret_cast<const uint4*>(a.kp + (static_cast<int64_t>(page) * a.n_kv + kvh) * 16 * D);
-    const uint4* vsrc = reinterpret_cast<const uint4*>(a.vp + (static_cast<int64_t>(page) * a.n_kv + kvh) * 16 * D);
-    uint4 kreg[U4_PER_LANE], vreg[U4_PER_LANE];
+  // page pg of this wave: physical id and its K/V rows, one page ahead
+  auto page_id = [&](int pg) -> int {
+    const int id = a.pt[static_cast<int64_t>(b) * a.max_pages + pg];
+    return (id >= 0 && id < a.num_pages) ? id : -1;
+  };
+  u32x4 kreg[U4], vreg[U4];
+  int pg = p0 + w;
+  int cur = pg < p1 ? page_id(pg) : -1;
+  if (cur >= 0) {
+    const u32x4* ks = reinterpret_cast<const u32x4*>(a.kp + (static_cast<int64_t>(cur) * a.n_kv + kvh) * 16 * D);
+    const u32x4* vs = reinterpret_cast<const u32x4*>(a.vp + (static_cast<int64_t>(cur) * a.n_kv + kvh) * 16 * D);
 #pragma unroll
-    for (int i = 0; i < U4_PER_LANE; ++i) {
-      kreg[i] = ksrc[i * 64 + lane];
-      vreg[i] = vsrc[i * 64 + lane];
-    }
-    wave_sync();  // every lane is done with the previous page's LDS
-#pragma unroll
-    for (int i = 0; i < U4_PER_LANE; ++i) {
-      reinterpret_cast<uint4*>(lk[w])[i * 64 + lane] = kreg[i];
-      reinterpret_cast<uint4*>(lv[w])[i * 64 + lane] = vreg[i];
-    }
-    wave_sync();
-
-    // scores: lane (t, c) covers token t, dims [c*DC, c*DC + DC)
-    float sc[REP];
-    const uint4* kr = reinterpret_cast<const uint4*>(lk[w] + t * D + c * DC);
-#pragma unroll
-    for (int h = 0; h < REP; ++h) sc[h] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < DC / 8; ++j) {
-      const uint4 kk = kr[j];
-#pragma unroll
-      for (int h = 0; h < REP; ++h) {
-        sc[h] = dot2(qr[h][4 * j + 0], kk.x, sc[h]);
-        sc[h] = dot2(qr[h][4 * j + 1], kk.y, sc[h]);
-        sc[h] = dot2(qr[h][4 * j + 2], kk.z, sc[h]);
-        sc[h] = dot2(qr[h][4 * j + 3], kk.w, sc[h]);
-      }
-    }
-    float pr[REP];
-#pragma unroll
-    for (int h = 0; h < REP; ++h) {
-      float v = sc[h];
-      v += __shfl_xor(v, 1);
-      v += __shfl_xor(v, 2);
-      v = (t < valid) ? v * scale : -INFINITY;
-      float mx = v;
-      mx = fmaxf(mx, __shfl_xor(mx, 4));
-      mx = fmaxf(mx, __shfl_xor(mx, 8));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[h], mx);
-      const float alpha = expf(m[h] - mnew);
-      pr[h] = expf(v - mnew);
-      l[h] = l[h] * alpha + (c == 0 ? pr[h] : 0.0f);
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) o[h][e] *= alpha;
-      m[h] = mnew;
-    }
-    if (c == 0) {
-#pragma unroll
-      for (int h = 0; h < REP; ++h) lp[w][h][t] = pr[h];
-    }
-    wave_sync();
-    // PV: lane owns dims [lane*DPL, lane*DPL + DPL)
-#pragma unroll 4
-    for (int t2 = 0; t2 < kPageTokens; ++t2) {
-      float vv[DPL];
-      if (DPL == 2) {
-        const h2 v2 = *reinterpret_cast<const h2*>(lv[w] + t2 * D + lane * 2);
-        vv[0] = static_cast<float>(v2[0]);
-        vv[DPL - 1] = static_cast<float>(v2[1]);
-      } else {
-        vv[0] = static_cast<float>(lv[w][t2 * D + lane]);
-      }
-      const bool ok = t2 < valid;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) vv[e] = ok ? vv[e] : 0.0f;
-#pragma unroll
-      for (int h = 0; h < REP; ++h) {
-        const float pv = lp[w][h][t2];
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) o[h][e] = fmaf(pv, vv[e], o[h][e]);
-      }
+    for (int i = 0; i < U4; ++i) {
+      kreg[i] = ks[i * 64 + lane];
+      vreg[i] = vs[i * 64 + lane];
     }
   }
+  for (; pg < p1; pg += NW) {  // wave-uniform trip count, no block barrier inside
+    if (cur < 0) {
+      if (lane == 0) raise_flag(a.err, 2);
+    }
+    wave_sync();  // every lane is done with the previous page's LDS
+    if (cur >= 0) {
+#pragma unroll
+      for (int i = 0; i < U4; ++i) {
+        reinterpret_cast<u32x4*>(lk[w])[i * 64 + lane] = kreg[i];
+        reinterpret_cast<u32x4*>(lv[w])[i * 64 + lane] = vreg[i];
+      }
+    }
+    const int valid = cur >= 0 ? min(kPageTokens, len - pg * kPageTokens) : 0;
+    // issue the next page's loads before computing this one
+    const int nxt = pg + NW < p1 ? page_id(pg + NW) : -1;
+    if (nxt >= 0) {
+      const u32x4* ks = reinterpret_cast<const u32x4*>(a.kp + (static_cast<int64_t>(nxt) * a.n_kv + kvh) * 16 * D);
+      const u32x4* vs = reinterpret_cast<const u32x4*>(a.vp + (static_cast<int64_t>(nxt) * a.n_kv + kvh) * 16 * D);
+#pragma unroll
+      for (int i = 0; i < U4; ++i) {
+        kreg[i] = ks[i * 64 + lane];
+        vreg[i] = vs[i * 64 + lane];
+      }
+    }
+    wave_sync();
+    if (valid > 0) {
+      // scores: lane (t, c) covers token t, dims [c*DC, c*DC + DC)
+      float sc[REP];
+      const u32x4* kr = reinterpret_cast<const u32x4*>(lk[w] + t * D + c * DC);
+#pragma unroll
+      for (int h = 0; h < REP; ++h) sc[h] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < DC / 8; ++j) {
+        const u32x4 kk = kr[j];
+#pragma unroll
+        for (int h = 0; h < REP; ++h) {
+          sc[h] = dot2(qr[h][4 * j + 0], kk[0], sc[h]);
+          sc[h] = dot2(qr[h][4 * j + 1], kk[1], sc[h]);
+          sc[h] = dot2(qr[h][4 * j + 2], kk[2], sc[h]);
+          sc[h] = dot2(qr[h][4 * j + 3], kk[3], sc[h]);
+        }
+      }
+      float pr[REP];
+#pragma unroll
+      for (int h = 0; h < REP; ++h) {
+        float v = sc[h];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v = (t < valid) ? v * scale : -INFINITY;
+        float mx = v;
+        mx = fmaxf(mx, __shfl_xor(mx, 4));
+        mx = fmaxf(mx, __shfl_xor(mx, 8));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m[h], mx);
+        const float alpha = expf(m[h] - mnew);
+        pr[h] = expf(v - mnew);
+        l[h] = l[h] * alpha + (c == 0 ? pr[h] : 0.0f);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[h][e] *= alpha;
+        m[h] = mnew;
+      }
+      if (c == 0) {
+#pragma unroll
+        for (int h = 0; h < REP; ++h) lp[w][h][t] = pr[h];
+      }
+      wave_sync();
+      // PV: lane owns dims [lane*DPL, lane*DPL + DPL)
+#pragma unroll 4
+      for (int t2 = 0; t2 < kPageTokens; ++t2) {
+        float vv[DPL];
+        if constexpr (DPL == 2) {
+          const h2 v2 = *reinterpret_cast<const h2*>(lv[w] + t2 * D + lane * 2);
+          vv[0] = static_cast<float>(v2[0]);
+          vv[DPL - 1] = static_cast<float>(v2[1]);
+        } else {
+          vv[0] = static_cast<float>(lv[w][t2 * D + lane]);
+        }
+        const bool ok = t2 < valid;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) vv[e] = ok ? vv[e] : 0.0f;
+#pragma unroll
+        for (int h = 0; h < REP; ++h) {
+          const float pv = lp[w][h][t2];
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) o[h][e] = fmaf(pv, vv[e], o[h][e]);
+        }
+      }
+    }
+    cur = nxt;
+  }
 
-  // combine the four waves (uniform control flow: every wave reaches the barrier)
+  // combine the waves (uniform control flow: every wave reaches the barrier)
 #pragma unroll
   for (int h = 0; h < REP; ++h) {
     float v = l[h];
@@ -569,57 +799,59 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams a) {
     for (int e = 0; e < DPL; ++e) red_o[w][h][lane * DPL + e] = o[h][e];
   }
   __syncthreads();
-  for (int i = tid; i < REP * D; i += 256) {
+  const int64_t row0 = (static_cast<int64_t>(b) * a.n_heads + kvh * REP) * a.S;
+  for (int i = tid; i < REP * D; i += 64 * NW) {
     const int h = i / D, d = i % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, red_m[ww][h]);
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, red_m[ww][h]);
     float L = 0.0f, O = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       const float f = (red_m[ww][h] == -INFINITY) ? 0.0f : expf(red_m[ww][h] - M);
       L = fmaf(f, red_l[ww][h], L);
       O = fmaf(f, red_o[ww][h][d], O);
     }
-    const int64_t row = (static_cast<int64_t>(b) * a.n_heads + kvh * REP + h) * a.S + s;
-    a.po[row * D + d] = O;
-    if (d == 0) {
-      a.pml[row * 2] = M;
-      a.pml[row * 2 + 1] = L;
+    if (nact == 1) {
+      a.out[(static_cast<int64_t>(b) * a.n_heads + kvh * REP + h) * D + d] = static_cast<half_t>(L > 0.0f ? O / L : 0.0f);
+    } else {
+      const int64_t row = row0 + static_cast<int64_t>(h) * a.S + s;
+      a.po[row * D + d] = O;
+      if (d == 0) {
+        a.pml[row * 2] = M;
+        a.pml[row * 2 + 1] = L;
+      }
     }
   }
 }
 
-// grid (n_heads, B), D threads
+// grid (n_heads, B), D threads: merge the split partials of one query head.
 template <int D>
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams a) {
+  __shared__ float wgt[kMaxSplits];
+  __shared__ float inv_l;
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int len = a.lens[b] + a.len_add;
-  half_t* out = a.out + (static_cast<int64_t>(b) * a.n_heads + h) * D;
-  if (len <= 0) {
-    out[d] = static_cast<half_t>(0.0f);
-    return;
+  int npages, per, nact;
+  split_geometry(len, a.max_pages, a.S, npages, per, nact);
+  if (len <= 0 || nact <= 1) return;  // the split kernel wrote the output
+  const int64_t rb = (static_cast<int64_t>(b) * a.n_heads + h) * a.S;
+  if (d < 64) {  // one wave: max and softmax weights of the splits
+    const float m0 = d < nact ? a.pml[(rb + d) * 2] : -INFINITY;
+    const float l0 = d < nact ? a.pml[(rb + d) * 2 + 1] : 0.0f;
+    float M = m0;
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float f = (m0 == -INFINITY) ? 0.0f : expf(m0 - M);
+    float L = f * l0;
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+    if (d < nact) wgt[d] = f;
+    if (d == 0) inv_l = L > 0.0f ? 1.0f / L : 0.0f;
   }
-  int npages = min((len + kPageTokens - 1) / kPageTokens, a.max_pages);
-  const int per = max(kMinPagesPerSplit, (npages + a.S - 1) / a.S);
-  const int nact = (npages + per - 1) / per;
-  const int64_t row0 = (static_cast<int64_t>(b) * a.n_heads + h) * a.S;
-  float M = -INFINITY;
-  for (int s = 0; s < nact; ++s) M = fmaxf(M, a.pml[(row0 + s) * 2]);
-  float L = 0.0f, O = 0.0f;
-  for (int s = 0; s < nact; ++s) {
-    const float ms = a.pml[(row0 + s) * 2];
-    const float f = (ms == -INFINITY) ? 0.0f : expf(ms - M);
-    L = fmaf(f, a.pml[(row0 + s) * 2 + 1], L);
-    O = fmaf(f, a.po[(row0 + s) * D + d], O);
-  }
-  out[d] = static_cast<half_t>(L > 0.0f ? O / L : 0.0f);
-}
-
-template <int D, int REP>
-static void launch_attn_t(const AttnParams& p, int batch, hipStream_t s) {
-  attn_split_kernel<D, REP><<<dim3(p.S, p.n_kv, batch), dim3(256), 0, s>>>(p);
-  attn_combine_kernel<D><<<dim3(p.n_heads, batch), dim3(D), 0, s>>>(p);
+  __syncthreads();
+  float O = 0.0f;
+#pragma unroll 8
+  for (int s = 0; s < nact; ++s) O = fmaf(wgt[s], a.po[(rb + s) * D + d], O);
+  a.out[(static_cast<int64_t>(b) * a.n_heads + h) * D + d] = static_cast<half_t>(O * inv_l);
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
@@ -640,8 +872,13 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   p.S = a.splits;
   p.err = a.err;
   const int rep = a.n_heads / a.n_kv;
-#define NQ_ATT(DD, RR) \
-  if (a.head_dim == DD && rep == RR) { launch_attn_t<DD, RR>(p, a.batch, s); return hipGetLastError(); }
+  const dim3 grid(p.S, p.n_kv, a.batch), block(64 * kAttnWaves);
+#define NQ_ATT(DD, RR)                                                                   \
+  if (a.head_dim == DD && rep == RR) {                                                   \
+    attn_decode_kernel<DD, RR><<<grid, block, 0, s>>>(p);                                \
+    attn_combine_kernel<DD><<<dim3(a.n_heads, a.batch), dim3(DD), 0, s>>>(p);            \
+    return hipGetLastError();                                                            \
+  }
   NQ_ATT(128, 7) NQ_ATT(128, 8) NQ_ATT(128, 4) NQ_ATT(128, 2) NQ_ATT(128, 1)
   NQ_ATT(64, 4) NQ_ATT(64, 7) NQ_ATT(64, 8) NQ_ATT(64, 2) NQ_ATT(64, 1)
 #undef NQ_ATT
@@ -686,64 +923,55 @@ hipError_t launch_kv_append(void* k_pool, void* v_pool, int32_t batch, int32_t n
   return hipGetLastError();
 }
 
-__global__ void embed_kernel(const half_t* E, int vocab, int H, const int32_t* tokens, half_t* h,
-                             int32_t* err) {
-  const int b = blockIdx.x;
-  int tok = tokens[b];
-  if (tok < 0 || tok >= vocab) {
-    if (threadIdx.x == 0) raise_flag(err, 4);
-    tok = 0;
-  }
-  const uint4* src = reinterpret_cast<const uint4*>(E + static_cast<int64_t>(tok) * H);
-  uint4* dst = reinterpret_cast<uint4*>(h + static_cast<int64_t>(b) * H);
-  for (int i = threadIdx.x; i < H / 8; i += blockDim.x) dst[i] = src[i];
-}
-
-hipError_t launch_embed(const void* embed, int32_t vocab, int32_t hidden, const int32_t* tokens,
-                        int32_t batch, void* h, int32_t* err, hipStream_t s) {
-  embed_kernel<<<dim3(batch), dim3(256), 0, s>>>(static_cast<const half_t*>(embed), vocab, hidden, tokens,
-                                                 static_cast<half_t*>(h), err);
-  return hipGetLastError();
-}
-
-// grid (B), 256 threads: reduce per-tile (max, lowest index) partials.
-__global__ __launch_bounds__(256) void argmax_finalize_kernel(const float* vals, const int32_t* idx,
-                                                              int T, int* tokens, int* pos, int* hist,
-                                                              int hist_len) {
-  __shared__ float sv[256];
-  __shared__ int si[256];
-  const int b = blockIdx.x, tid = threadIdx.x;
+// grid (B), 1024 threads: reduce the LM head's per-workgroup (max, index)
+// partials of one batch row, write the greedy token, its history entry, and
+// advance the position.
+__global__ __launch_bounds__(1024) void argmax_finalize_kernel(const float* vals, const int32_t* idx, int P,
+                                                               int32_t* tokens, int32_t* pos, int32_t* hist,
+                                                               int hist_len) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float best = -INFINITY;
   int bi = 0x7fffffff;
-  for (int t = tid; t < T; t += 256) {
-    const float v = vals[static_cast<int64_t>(b) * T + t];
-    const int i = idx[static_cast<int64_t>(b) * T + t];
-    if (v > best || (v == best && i < bi)) { best = v; bi = i; }
-  }
-  sv[tid] = best;
-  si[tid] = bi;
-  __syncthreads();
-  for (int off = 128; off >= 1; off >>= 1) {
-    if (tid < off) {
-      const float v = sv[tid + off];
-      const int i = si[tid + off];
-      if (v > sv[tid] || (v == sv[tid] && i < si[tid])) { sv[tid] = v; si[tid] = i; }
+  for (int i = tid; i < P; i += 1024) {
+    const float v = vals[static_cast<int64_t>(b) * P + i];
+    const int ix = idx[static_cast<int64_t>(b) * P + i];
+    if (better(v, ix, best, bi)) {
+      best = v;
+      bi = ix;
     }
-    __syncthreads();
   }
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float v = __shfl_xor(best, o);
+    const int ix = __shfl_xor(bi, o);
+    if (better(v, ix, best, bi)) {
+      best = v;
+      bi = ix;
+    }
+  }
+  if (lane == 0) {
+    sv[w] = best;
+    si[w] = bi;
+  }
+  __syncthreads();
   if (tid == 0) {
-    const int tok = si[0] == 0x7fffffff ? 0 : si[0];
-    const int p = pos[b];
+    for (int k = 1; k < static_cast<int>(blockDim.x >> 6); ++k)
+      if (better(sv[k], si[k], best, bi)) {
+        best = sv[k];
+        bi = si[k];
+      }
+    const int tok = bi == 0x7fffffff ? 0 : bi;
+    const int ps = pos[b];
     tokens[b] = tok;
-    if (hist && p + 1 >= 0 && p + 1 < hist_len) hist[static_cast<int64_t>(b) * hist_len + p + 1] = tok;
-    pos[b] = p + 1;
+    if (hist && ps + 1 >= 0 && ps + 1 < hist_len) hist[static_cast<int64_t>(b) * hist_len + ps + 1] = tok;
+    pos[b] = ps + 1;
   }
 }
 
-hipError_t launch_argmax_finalize(const float* vals, const int32_t* idx, int32_t tiles, int32_t batch,
-                                  int32_t /*vocab*/, int32_t* tokens, int32_t* pos, int32_t* hist,
-                                  int32_t hist_len, int32_t* /*err*/, hipStream_t s) {
-  argmax_finalize_kernel<<<dim3(batch), dim3(256), 0, s>>>(vals, idx, tiles, tokens, pos, hist, hist_len);
+hipError_t launch_argmax_finalize(const float* vals, const int32_t* idx, int32_t partials, int32_t batch,
+                                  int32_t* tokens, int32_t* pos, int32_t* hist, int32_t hist_len, hipStream_t s) {
+  argmax_finalize_kernel<<<dim3(batch), dim3(1024), 0, s>>>(vals, idx, partials, tokens, pos, hist, hist_len);
   return hipGetLastError();
 }
 

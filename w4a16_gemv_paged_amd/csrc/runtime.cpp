@@ -73,9 +73,9 @@ Workspace carve(const nq_config& c, int32_t batch, int32_t max_pages, uint8_t* b
   w.act = take(static_cast<size_t>(batch) * c.intermediate * 2);
   w.part_o = reinterpret_cast<float*>(take(static_cast<size_t>(batch) * c.n_heads * w.splits * c.head_dim * 4));
   w.part_ml = reinterpret_cast<float*>(take(static_cast<size_t>(batch) * c.n_heads * w.splits * 2 * 4));
-  const int64_t T = tiles_of(c.vocab);
-  w.amax_val = reinterpret_cast<float*>(take(static_cast<size_t>(batch) * T * 4));
-  w.amax_idx = reinterpret_cast<int32_t*>(take(static_cast<size_t>(batch) * T * 4));
+  const int64_t P = gemv_grid_size(c.vocab, c.hidden, batch);
+  w.amax_val = reinterpret_cast<float*>(take(static_cast<size_t>(batch) * P * 4));
+  w.amax_idx = reinterpret_cast<int32_t*>(take(static_cast<size_t>(batch) * P * 4));
   w.total = off;
   return w;
 }
@@ -124,9 +124,7 @@ int enqueue_step(nq_model* m, nq_kv* kv, const nq_step_io* io, hipStream_t s) {
   const size_t lp = layer_pool_elems(c, kv->num_pages);
   uint16_t* pool = static_cast<uint16_t*>(kv->pool);
   int launches = 0;
-  hipError_t e = launch_embed(m->embed, c.vocab, c.hidden, io->tokens, B, w.h, err, s);
-  if (e != hipSuccess) return hip_fail(e, "embed launch"), -1;
-  ++launches;
+  hipError_t e = hipSuccess;
   for (int l = 0; l < c.layers; ++l) {
     const nq_layer_ptrs& L = m->layers[l];
     uint16_t* kbase = pool + static_cast<size_t>(l) * 2 * lp;
@@ -140,6 +138,13 @@ int enqueue_step(nq_model* m, nq_kv* kv, const nq_step_io* io, hipStream_t s) {
     q.head_dim = c.head_dim;
     q.batch = B;
     q.x = w.h;
+    if (l == 0) {  // the embedding gather happens in this kernel's prologue
+      q.x = nullptr;
+      q.embed = m->embed;
+      q.tokens_in = io->tokens;
+      q.vocab = c.vocab;
+      q.h_out = w.h;
+    }
     q.norm_gain = L.attn_norm;
     q.eps = c.rms_eps;
     q.bias = L.qkv_bias;
@@ -233,8 +238,8 @@ int enqueue_step(nq_model* m, nq_kv* kv, const nq_step_io* io, hipStream_t s) {
   lm.amax_idx = w.amax_idx;
   lm.err = err;
   if ((e = launch_gemv(lm, s)) != hipSuccess) return hip_fail(e, "lm head launch"), -1;
-  e = launch_argmax_finalize(w.amax_val, w.amax_idx, static_cast<int32_t>(tiles_of(c.vocab)), B, c.vocab,
-                             io->tokens, io->pos, io->token_hist, io->hist_len, err, s);
+  e = launch_argmax_finalize(w.amax_val, w.amax_idx, gemv_grid_size(c.vocab, c.hidden, B), B, io->tokens, io->pos,
+                             io->token_hist, io->hist_len, s);
   if (e != hipSuccess) return hip_fail(e, "argmax launch"), -1;
   return launches + 2;
 }
@@ -368,8 +373,8 @@ nq_status nq_attn_decode(const nq_kv* kv, int32_t layer, int32_t batch, const vo
   a.head_dim = kv->cfg.head_dim;
   a.splits = attn_splits_for(max_pages);
   a.part_o = static_cast<float*>(workspace);
-  a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                       align256(static_cast<size_t>(batch) * a.n_heads * a.splits * a.head_dim * 4));
+  const size_t o_bytes = align256(static_cast<size_t>(batch) * a.n_heads * a.splits * a.head_dim * 4);
+  a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + o_bytes);
   a.err = err_flag;
   hipError_t e = launch_attention(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");

@@ -42,19 +42,28 @@ class DeviceModel:
         self.cfg = NQConfig.from_shape(shape, max_batch, max_pos)
         self.handle = nq_model_create(self.cfg)
         self._keep = []
+        self.layers = []
         d = shape.head_dim
-        for li in range(shape.layers):
-            p = layer_params(li)
-            qkv = nq_pack_weights(np.concatenate([p["wq"], p["wk"], p["wv"]]), NQ_MAT_QKV, d)
-            o = nq_pack_weights(p["wo"], NQ_MAT_PLAIN)
-            gu = nq_pack_weights(np.concatenate([p["wg"], p["wu"]]), NQ_MAT_GATE_UP)
-            dn = nq_pack_weights(p["wd"], NQ_MAT_PLAIN)
-            bias = np.concatenate([p["bq"], p["bk"], p["bv"]]).astype(np.float16)
-            ts = [to_device(qkv, device), _f16_dev(bias, device), to_device(o, device), to_device(gu, device),
-                  to_device(dn, device), _f16_dev(p["g1"], device), _f16_dev(p["g2"], device)]
-            self._keep.extend(ts)
-            nq_model_bind_layer(self.handle, li, NQLayerPtrs(*[t.data_ptr() for t in ts]))
-            del p, qkv, o, gu, dn
+        # draw layer l+1 on a helper thread while layer l is packed and uploaded
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(1) as ex:
+            nxt = ex.submit(layer_params, 0)
+            for li in range(shape.layers):
+                p = nxt.result()
+                if li + 1 < shape.layers:
+                    nxt = ex.submit(layer_params, li + 1)
+                qkv = nq_pack_weights(np.concatenate([p["wq"], p["wk"], p["wv"]]), NQ_MAT_QKV, d)
+                o = nq_pack_weights(p["wo"], NQ_MAT_PLAIN)
+                gu = nq_pack_weights(np.concatenate([p["wg"], p["wu"]]), NQ_MAT_GATE_UP)
+                dn = nq_pack_weights(p["wd"], NQ_MAT_PLAIN)
+                bias = np.concatenate([p["bq"], p["bk"], p["bv"]]).astype(np.float16)
+                names = ("qkv", "bias", "o", "gate_up", "down", "g1", "g2")
+                ts = [to_device(qkv, device), _f16_dev(bias, device), to_device(o, device), to_device(gu, device),
+                      to_device(dn, device), _f16_dev(p["g1"], device), _f16_dev(p["g2"], device)]
+                self._keep.extend(ts)
+                self.layers.append(dict(zip(names, ts)))
+                nq_model_bind_layer(self.handle, li, NQLayerPtrs(*[t.data_ptr() for t in ts]))
+                del p, qkv, o, gu, dn
         self.embed = _f16_dev(head["embed"], device)
         self.g_final = _f16_dev(head["g_final"], device)
         self.lm = to_device(nq_pack_weights(head["lm_head"], NQ_MAT_LM_HEAD), device)
@@ -110,9 +119,8 @@ class Stepper:
         self.layer_out = (torch.empty(cfg.layers, self.batch, cfg.hidden, dtype=torch.float16, device=dev)
                           if want_layers else None)
         self.hist = torch.full((self.batch, hist_len), -1, dtype=torch.int32, device=dev) if hist_len else None
-        wsb = nq_workspace_bytes(cfg, self.batch, self.max_pages)
-        self.ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
-        nq_model_bind_workspace(model.handle, self.ws, wsb)
+        self.ws_bytes = nq_workspace_bytes(cfg, self.batch, self.max_pages)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)
         p = lambda t: t.data_ptr() if t is not None else None
         self.io = NQStepIO(self.batch, self.max_pages, p(self.page_table), p(self.tokens), p(self.pos),
                            p(self.logits), p(self.layer_out), p(self.hist), hist_len, p(self.err))
@@ -125,9 +133,11 @@ class Stepper:
         self.pos.copy_(torch.as_tensor(np.asarray(pos, np.int32)), non_blocking=False)
 
     def step(self, stream=None):
+        nq_model_bind_workspace(self.model.handle, self.ws, self.ws_bytes)
         nq_decode_step(self.model.handle, self.kv.handle, self.io, stream)
 
     def capture(self, stream):
+        nq_model_bind_workspace(self.model.handle, self.ws, self.ws_bytes)
         self.graph = nq_graph_capture(self.model.handle, self.kv.handle, self.io, stream)
         return nq_graph_kernel_count(self.graph)
 

@@ -255,12 +255,14 @@ class OracleLayer:
     """One decoder layer: quantised fused QKV [Wq; Wk; Wv] with bias, O,
     fused gate/up [Wg; Wu], down, and the two RMSNorm gains."""
 
-    def __init__(self, p: dict):
-        self.q_qkv, self.s_qkv = quantize_w4(np.concatenate([p["wq"], p["wk"], p["wv"]], axis=0))
+    def __init__(self, p: dict, quant=quantize_w4):
+        """``quant`` maps a float32 [N, K] matrix to (codes, scales); any
+        replacement must equal quantize_w4 (e.g. it applied to row blocks)."""
+        self.q_qkv, self.s_qkv = quant(np.concatenate([p["wq"], p["wk"], p["wv"]], axis=0))
         self.b_qkv = np.concatenate([p["bq"], p["bk"], p["bv"]]).astype(F16)
-        self.q_o, self.s_o = quantize_w4(p["wo"])
-        self.q_gu, self.s_gu = quantize_w4(np.concatenate([p["wg"], p["wu"]], axis=0))
-        self.q_d, self.s_d = quantize_w4(p["wd"])
+        self.q_o, self.s_o = quant(p["wo"])
+        self.q_gu, self.s_gu = quant(np.concatenate([p["wg"], p["wu"]], axis=0))
+        self.q_d, self.s_d = quant(p["wd"])
         self.g1 = np.asarray(p["g1"], F16)
         self.g2 = np.asarray(p["g2"], F16)
         self._w = {}
@@ -280,10 +282,10 @@ class OracleLayer:
 class OracleHead:
     """Embedding (fp16, untied), final RMSNorm gain and quantised LM head."""
 
-    def __init__(self, h: dict):
+    def __init__(self, h: dict, quant=quantize_w4):
         self.embed = np.asarray(h["embed"], F16)
         self.g_final = np.asarray(h["g_final"], F16)
-        self.q_lm, self.s_lm = quantize_w4(h["lm_head"])
+        self.q_lm, self.s_lm = quant(h["lm_head"])
         self._w = None
 
     def w_lm(self) -> np.ndarray:

@@ -35,6 +35,18 @@ def rel_inf(gpu, ref) -> float:
     return float(np.max(np.abs(g - r)) / (den if den > 0 else 1.0))
 
 
+def quantize_rows(w, chunk=8192, workers=8):
+    """oracle.quantize_w4 applied to row blocks on threads. Groups run along K
+    inside one row, so the result is the same as one call on the whole matrix
+    (checked by test_host_lib); it only saves time on 7B-sized matrices."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    blocks = [w[i:i + chunk] for i in range(0, w.shape[0], chunk)]
+    with ThreadPoolExecutor(workers) as ex:
+        parts = list(ex.map(oracle.quantize_w4, blocks))
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+
 def exact_case_weights(n, k, seed):
     """w = q * 2^-e with q in [-7, 7] (every group reaching |q| = 7) and e in
     [4, 8]: the quantiser gives back exactly (q, 2^-e)."""

@@ -1,0 +1,92 @@
+"""GPU decode parity at the full Qwen2.5-Coder-7B shape (28 layers, hidden 3584,
+28/4 heads of dim 128, vocab 152064), the launch configuration bench.py times.
+
+The full oracle run of a 7B-shaped model is too slow for a test, so the run is
+short (24 prompt tokens + 8 generated) and checked on samples the oracle can
+afford: three layers recomputed teacher-forced from the GPU's own layer inputs
+(first, middle, last), and the LM head + greedy choice recomputed from the
+GPU's final hidden state at every generated step over the full vocabulary."""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle.model import OracleLayer, Dims, layer_causal
+from w4a16_gemv_paged_amd.engine import DeviceModel, KVCache, Stepper, run_greedy
+from gpu_util import quantize_rows, rel_inf, say
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+SHAPE = synth.QWEN7B
+PROMPT, GEN = 24, 8
+LAYERS = (0, 13, 27)
+TOL_LAYER, TOL_LOGITS, MARGIN = 2e-3, 5e-3, 1e-2
+
+
+@pytest.fixture(scope="module")
+def run7b():
+    say("build 7B device model")
+    head = synth.head_params(SHAPE, seed=0)
+    dm = DeviceModel(SHAPE, lambda l: synth.layer_params(SHAPE, l, seed=0), head, max_batch=8, max_pos=4096)
+    prompt = synth.prompt_ids(PROMPT, SHAPE.vocab, seed=2)
+    pt, total = synth.decode_page_tables(1, 4, seed=3, spare_pages=2)
+    out = {}
+    for graph in (False, True):
+        say("7B run", "graph" if graph else "eager")
+        kv = KVCache(dm, total, poison=True)
+        st = Stepper(dm, kv, pt, want_logits=True, want_layers=True)
+        stream = torch.cuda.Stream() if graph else torch.cuda.current_stream()
+        with torch.cuda.stream(stream):
+            out[graph] = run_greedy(st, [prompt], GEN, use_graph=graph, stream=stream, record_logits=True,
+                                    record_layers=True)
+        torch.cuda.synchronize()
+        st.close()
+        kv.close()
+    dm.close()
+    del dm
+    torch.cuda.empty_cache()
+    return prompt, head, out[False], out[True]
+
+
+def test_7b_graph_equals_eager(run7b):
+    prompt, head, eager, graph = run7b
+    np.testing.assert_array_equal(graph["tokens"], eager["tokens"])
+    np.testing.assert_array_equal(graph["logits"].view(np.uint32), eager["logits"].view(np.uint32))
+    np.testing.assert_array_equal(graph["layer_out"].view(np.uint16), eager["layer_out"].view(np.uint16))
+
+
+def test_7b_layers_teacher_forced(run7b):
+    prompt, head, gpu, _ = run7b
+    fed = list(prompt) + list(gpu["tokens"][0][:-1])
+    lo = gpu["layer_out"][:, :, 0]                                   # [T, L, H]
+    dims = Dims(SHAPE.hidden, SHAPE.intermediate, SHAPE.n_heads, SHAPE.n_kv_heads, SHAPE.head_dim, SHAPE.vocab)
+    with ThreadPoolExecutor(len(LAYERS)) as ex:
+        layers = list(ex.map(lambda l: OracleLayer(synth.layer_params(SHAPE, l, seed=0), quant=quantize_rows), LAYERS))
+    for li, L in zip(LAYERS, layers):
+        say("oracle layer", li)
+        x = head["embed"][np.array(fed)] if li == 0 else lo[:, li - 1]
+        ref = layer_causal(L, dims, x)
+        errs = [rel_inf(lo[t, li], ref[t]) for t in range(len(fed))]
+        assert max(errs) < TOL_LAYER, (li, max(errs))
+        L.drop_cache()
+
+
+def test_7b_head_logits_and_tokens(run7b):
+    prompt, head, gpu, _ = run7b
+    q, s = quantize_rows(head["lm_head"])
+    w = oracle.dequantize_w4(q, s)
+    hfin = gpu["layer_out"][:, -1, 0]                               # [T, H] after the last layer
+    x = oracle.rmsnorm(hfin, head["g_final"], 1e-6).astype(np.float64)
+    steps = range(PROMPT - 1, PROMPT - 1 + GEN)
+    clear = 0
+    for i, t in enumerate(steps):
+        z = w @ x[t]
+        assert rel_inf(gpu["logits"][t, 0], z) < TOL_LOGITS
+        top2 = np.sort(z)[-2:]
+        if top2[1] - top2[0] > MARGIN:
+            clear += 1
+            assert gpu["tokens"][0][i] == oracle.argmax_lowest(z), (i, t)
+    assert clear >= GEN // 2

@@ -122,3 +122,14 @@ def test_planted_bad_divisor_is_caught(monkeypatch):
     q = np.clip(np.rint(w.reshape(8, 2, 128) / s.astype(np.float64)[:, :, None]), -8, 7)
     err = np.abs(w.reshape(8, 2, 128) - q * s.astype(np.float64)[:, :, None])
     assert np.any(err > s.astype(np.float64)[:, :, None] / 2)
+
+
+def test_row_block_quantiser_equals_whole_matrix_call():
+    """The threaded row-block helper used by the 7B tests gives exactly the
+    oracle's codes and scales (groups never cross rows)."""
+    from gpu_util import quantize_rows
+    w = np.random.default_rng(11).standard_normal((77, 384)).astype(np.float32)
+    q0, s0 = quantize_w4(w)
+    q1, s1 = quantize_rows(w, chunk=10, workers=3)
+    np.testing.assert_array_equal(q0, q1)
+    np.testing.assert_array_equal(s0.view(np.uint16), s1.view(np.uint16))

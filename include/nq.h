@@ -190,11 +190,13 @@ nq_status nq_config_check(const nq_config* cfg);
 /*
  * Paged KV cache ("What it actually builds": 16 tokens per 4 KiB page, pages
  * reached through a page table). The pool is caller-owned device memory:
- *   pool[layer][0 = K, 1 = V][page][kv_head][slot 0..15][head_dim]  fp16
+ *   pool[layer][0 = K][page][kv_head][slot 0..15][head_dim]  fp16 (token-major)
+ *   pool[layer][1 = V][page][kv_head][head_dim][slot 0..15]  fp16 (dim-major)
  * so one (layer, K or V, page, kv_head) block is 16 * head_dim fp16 (4096 bytes
  * at head_dim 128). Token p of sequence b is in page page_table[b][p / 16],
  * slot p % 16. Page ids are chosen by the caller (any permutation of the pool;
- * -1 marks an unused table entry). K is stored after RoPE.
+ * -1 marks an unused table entry). K is stored after RoPE. V is dim-major so
+ * that the attention's P.V product reads it in matrix-core operand order.
  */
 typedef struct nq_kv nq_kv;
 
@@ -207,7 +209,8 @@ nq_status nq_kv_alloc(const nq_config* cfg, void* pool_dev, size_t bytes,
 
 /*
  * Writes one token's K and V per sequence into the pool:
- *   pool[layer][0][pt[b][pos[b]/16]][h][pos[b]%16][:] = k[b][h][:]  (and V likewise)
+ *   pool[layer][0][pt[b][pos[b]/16]][h][pos[b]%16][:] = k[b][h][:]
+ *   pool[layer][1][pt[b][pos[b]/16]][h][:][pos[b]%16] = v[b][h][:]
  * page_table: device int32 [batch][max_pages]; pos: device int32 [batch];
  * k, v: device fp16 [batch][n_kv_heads][head_dim].
  * err_flag: optional device int32; a position beyond max_pages*16, or a page id
@@ -235,6 +238,7 @@ size_t nq_attn_workspace_bytes(const nq_config* cfg, int32_t batch, int32_t max_
  * are never used, whatever they hold.
  * q: device fp16 [batch][n_heads][head_dim]; out: device fp16, same shape.
  * lens: device int32 [batch] (0 gives a zero output row).
+ * max_pages: page_table row stride, 1..32768 (NQ_ERR_OUT_OF_RANGE beyond).
  * workspace: device, nq_attn_workspace_bytes(cfg, batch, max_pages) bytes for
  * the split partials; calls that share a workspace must not overlap.
  * err_flag: optional device int32 (bad page id or length -> ORs 2, output 0).
@@ -283,7 +287,7 @@ void nq_model_destroy(nq_model* m);
 
 typedef struct nq_step_io {
   int32_t batch;            /* 1 .. cfg.max_batch                                          */
-  int32_t max_pages;        /* page_table row stride (pages per sequence)                  */
+  int32_t max_pages;        /* page_table row stride (pages per sequence), 1..32768        */
   const int32_t* page_table;/* device int32 [batch][max_pages]                             */
   int32_t* tokens;          /* device int32 [batch]: in = token at pos, out = greedy next  */
   int32_t* pos;             /* device int32 [batch]: in = position of the input token;
@@ -306,8 +310,9 @@ typedef struct nq_step_io {
  * O GEMV + residual -> RMSNorm -> gate/up GEMV + SwiGLU -> down GEMV +
  * residual; final RMSNorm -> LM-head GEMV -> argmax (lowest index on ties)
  * -> tokens, pos += 1. That is 6 kernels per layer (attention is a split
- * kernel and a combine kernel) plus 2 (LM head, argmax); the gather runs in
- * layer 0's QKV kernel.
+ * kernel and a combine kernel; 5 when max_pages is small enough that one
+ * workgroup covers a sequence's pages) plus 2 (LM head, argmax); the gather
+ * runs in layer 0's QKV kernel.
  * Errors: NQ_ERR_STATE if the model is not fully bound; NQ_ERR_INVALID_ARG for
  * bad io; NQ_ERR_HIP on launch failure.
  */

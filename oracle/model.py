@@ -180,17 +180,22 @@ class PagedKVEmu:
     """Paged cache ("What it actually builds": 16 tokens per page, pages are
     non-contiguous blocks found through a page table).
 
-    Pool layout [layer][K=0 / V=1][page][kv_head][slot (16)][d] fp16, so one
-    page of one KV head holds 16 x d fp16 (4 KiB at d = 128). Token p of
-    sequence b lives in page page_table[b][p // 16], slot p % 16. The pool
+    Pool layout [layer][K=0 / V=1][page][kv_head][16 * d] fp16: one page of one
+    KV head holds 16 tokens x d fp16 (4 KiB at d = 128). The pages fix only the
+    page size, so the order inside a page is a reading: K is token-major
+    (element slot * d + e) and V is dim-major (element e * 16 + slot). Token p
+    of sequence b lives in page page_table[b][p // 16], slot p % 16. The pool
     starts filled with NaN so that a read of a slot never written shows up."""
 
     def __init__(self, layers: int, num_pages: int, n_kv: int, d: int,
                  page_table, page_tokens: int = 16, pool=None):
         self.page_tokens = page_tokens
+        self.d = d
         self.pt = np.asarray(page_table, dtype=np.int32)
         if pool is None:
-            pool = np.full((layers, 2, num_pages, n_kv, page_tokens, d), np.nan, dtype=F16)
+            pool = np.full((layers, 2, num_pages, n_kv, page_tokens * d), np.nan, dtype=F16)
+        if pool.shape[-1] != page_tokens * d:
+            raise ValueError("pool pages must hold page_tokens * d elements per KV head")
         self.pool = pool
 
     def locate(self, b: int, pos: int):
@@ -203,31 +208,35 @@ class PagedKVEmu:
         return page, pos % self.page_tokens
 
     def append(self, layer: int, b: int, pos: int, k16, v16) -> None:
+        """k16, v16 [n_kv, d] of token ``pos``."""
         page, slot = self.locate(b, pos)
-        self.pool[layer, 0, page, :, slot, :] = k16
-        self.pool[layer, 1, page, :, slot, :] = v16
+        d, T = self.d, self.page_tokens
+        self.pool[layer, 0, page, :, slot * d:(slot + 1) * d] = k16
+        self.pool[layer, 1, page, :, slot::T] = v16
 
     def get(self, layer: int, b: int, length: int):
-        npages = (length + self.page_tokens - 1) // self.page_tokens
+        """K and V of positions 0..length-1 as [length, n_kv, d]."""
+        T, d = self.page_tokens, self.d
+        npages = (length + T - 1) // T
         ids = self.pt[b, :npages]
         if np.any(ids < 0) or np.any(ids >= self.pool.shape[2]):
             raise IndexError("page table entry out of range")
-        k = self.pool[layer, 0, ids]            # [np, nkv, 16, d]
-        v = self.pool[layer, 1, ids]
-        k = k.transpose(0, 2, 1, 3).reshape(-1, k.shape[1], k.shape[3])[:length]
-        v = v.transpose(0, 2, 1, 3).reshape(-1, v.shape[1], v.shape[3])[:length]
-        return k, v
+        nkv = self.pool.shape[3]
+        k = self.pool[layer, 0, ids].reshape(npages, nkv, T, d).transpose(0, 2, 1, 3)
+        v = self.pool[layer, 1, ids].reshape(npages, nkv, d, T).transpose(0, 3, 1, 2)
+        return (k.reshape(npages * T, nkv, d)[:length], v.reshape(npages * T, nkv, d)[:length])
 
 
 def paged_attention(q16, pool_layer, page_table, lens) -> np.ndarray:
     """Decode attention of B sequences over one layer's page pool.
 
-    q16 [B, nh, d]; pool_layer [2][P][nkv][16][d]; lens[b] = number of cached
-    tokens of sequence b. Returns float64 [B, nh, d]."""
+    q16 [B, nh, d]; pool_layer [2][P][nkv][16 * d] (PagedKVEmu layout);
+    lens[b] = number of cached tokens of sequence b. Returns float64 [B, nh, d]."""
     q16 = np.asarray(q16, dtype=F16)
     pool = np.asarray(pool_layer, dtype=F16)[None]
-    kv = PagedKVEmu(1, pool.shape[2], pool.shape[3], pool.shape[5], page_table,
-                    page_tokens=pool.shape[4], pool=pool)
+    d = q16.shape[-1]
+    kv = PagedKVEmu(1, pool.shape[2], pool.shape[3], d, page_table,
+                    page_tokens=pool.shape[4] // d, pool=pool)
     out = np.empty(q16.shape, dtype=F64)
     for b in range(q16.shape[0]):
         k, v = kv.get(0, b, int(lens[b]))

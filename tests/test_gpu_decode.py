@@ -113,7 +113,7 @@ def test_kv_pool_contents_and_untouched_slots(tiny_run, tiny):
     fed = list(prompt) + list(gpu["tokens"][0][:-1])
     T = len(fed)
     cfg = dm.cfg
-    pool = gpu["pool"].view(F16).reshape(cfg.layers, 2, -1, cfg.n_kv_heads, 16, cfg.head_dim)
+    pool = gpu["pool"].view(F16).reshape(cfg.layers, 2, -1, cfg.n_kv_heads, 16 * cfg.head_dim)
     kvm = oracle.PagedKVEmu(cfg.layers, pool.shape[2], cfg.n_kv_heads, cfg.head_dim, gpu["page_table"], pool=pool)
     lo = gpu["layer_out"][:, :, 0]
     x = om.head.embed[np.array(fed)]
@@ -128,8 +128,10 @@ def test_kv_pool_contents_and_untouched_slots(tiny_run, tiny):
         assert rel_inf(kg, k) < TOL_LAYER and rel_inf(vg, v) < TOL_LAYER
         x = lo[:, li]
     last_page = gpu["page_table"][0, (T - 1) // 16]
-    tail = pool[:, :, last_page, :, (T - 1) % 16 + 1:]
-    assert np.all(np.isnan(tail.astype(np.float32)))
+    s0 = (T - 1) % 16 + 1
+    kpage = pool[:, 0, last_page].reshape(cfg.layers, cfg.n_kv_heads, 16, d).astype(np.float32)
+    vpage = pool[:, 1, last_page].reshape(cfg.layers, cfg.n_kv_heads, d, 16).astype(np.float32)
+    assert np.all(np.isnan(kpage[:, :, s0:])) and np.all(np.isnan(vpage[..., s0:]))
 
 
 def test_token_history_written(tiny_run):
@@ -146,7 +148,7 @@ def test_graph_replay_equals_eager_bitwise(tiny, tiny_run):
     np.testing.assert_array_equal(g["tokens"], eager["tokens"])
     np.testing.assert_array_equal(g["logits"].view(np.uint32), eager["logits"].view(np.uint32))
     np.testing.assert_array_equal(g["layer_out"].view(np.uint16), eager["layer_out"].view(np.uint16))
-    assert g["kernels"] == 6 * SHAPE.layers + 2
+    assert g["kernels"] in (5 * SHAPE.layers + 2, 6 * SHAPE.layers + 2)   # attention combine only when split
 
 
 def test_batched_ragged_equals_single_sequences(tiny):

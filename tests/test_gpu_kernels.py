@@ -205,16 +205,11 @@ def _attn_setup(shape, lens, seed=5, perm_seed=3):
     inp = synth.attention_inputs(len(lens), shape.n_heads, shape.n_kv_heads, shape.head_dim, lens,
                                  seed=seed, perm_seed=perm_seed)
     cfg, pool, h = _kv_handle(shape, inp["num_pages"])
-    pool_np = np.full((1, 2, inp["num_pages"], shape.n_kv_heads, 16, shape.head_dim), np.nan, F16)
-    emu = oracle.PagedKVEmu(1, inp["num_pages"], shape.n_kv_heads, shape.head_dim, inp["page_table"], pool=pool_np)
+    emu = oracle.PagedKVEmu(1, inp["num_pages"], shape.n_kv_heads, shape.head_dim, inp["page_table"])
     for b, L in enumerate(lens):
-        pages = (L + 15) // 16
-        ids = inp["page_table"][b, :pages]
-        kk = np.full((pages * 16, shape.n_kv_heads, shape.head_dim), np.nan, F16)
-        vv = kk.copy()
-        kk[:L], vv[:L] = inp["k_tok"][b], inp["v_tok"][b]
-        pool_np[0, 0, ids] = kk.reshape(pages, 16, shape.n_kv_heads, shape.head_dim).transpose(0, 2, 1, 3)
-        pool_np[0, 1, ids] = vv.reshape(pages, 16, shape.n_kv_heads, shape.head_dim).transpose(0, 2, 1, 3)
+        for p in range(L):
+            emu.append(0, b, p, inp["k_tok"][b][p], inp["v_tok"][b][p])
+    pool_np = emu.pool
     layer_elems = pool_np[0, 0].size
     flat = pool.view(torch.float16)
     flat[: 2 * layer_elems].copy_(dev(pool_np[0].reshape(-1)))

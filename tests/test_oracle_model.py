@@ -42,8 +42,11 @@ def test_paged_run_equals_contiguous_run(micro):
     np.testing.assert_array_equal(a["logits"], b["logits"])
     # 16 + 8 - 1 = 23 positions written: page 0 full, page 1 has slots 0..6
     p1 = pt[0, 1]
-    assert not np.any(np.isnan(kv.pool[:, :, p1, :, :7].astype(np.float32)))
-    assert np.all(np.isnan(kv.pool[:, :, p1, :, 7:].astype(np.float32)))
+    d = MICRO.head_dim
+    kpage = kv.pool[:, 0, p1].reshape(MICRO.layers, MICRO.n_kv_heads, 16, d).astype(np.float32)
+    vpage = kv.pool[:, 1, p1].reshape(MICRO.layers, MICRO.n_kv_heads, d, 16).astype(np.float32)
+    assert not np.any(np.isnan(kpage[:, :, :7])) and np.all(np.isnan(kpage[:, :, 7:]))
+    assert not np.any(np.isnan(vpage[..., :7])) and np.all(np.isnan(vpage[..., 7:]))
 
 
 def test_run_convention_and_forcing(micro):

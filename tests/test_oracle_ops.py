@@ -224,13 +224,17 @@ def test_paged_attention_helper_matches_contiguous():
     B, nh, nkv, d = 2, 4, 2, 32
     lens = [19, 33]
     pt = np.array([[3, 0, -1], [4, 1, 2]], np.int32)
-    pool = np.full((2, 6, nkv, 16, d), np.nan, F16)
+    # the documented page layout written out by hand: K token-major, V dim-major
+    pool = np.full((2, 6, nkv, 16 * d), np.nan, F16)
     ks = [rng.standard_normal((L, nkv, d)).astype(F16) for L in lens]
     vs = [rng.standard_normal((L, nkv, d)).astype(F16) for L in lens]
     for b in range(B):
         for p in range(lens[b]):
-            pool[0, pt[b, p // 16], :, p % 16] = ks[b][p]
-            pool[1, pt[b, p // 16], :, p % 16] = vs[b][p]
+            page, slot = pt[b, p // 16], p % 16
+            for h in range(nkv):
+                for e in range(d):
+                    pool[0, page, h, slot * d + e] = ks[b][p, h, e]
+                    pool[1, page, h, e * 16 + slot] = vs[b][p, h, e]
     q = rng.standard_normal((B, nh, d)).astype(F16)
     out = oracle.paged_attention(q, pool, pt, lens)
     for b in range(B):

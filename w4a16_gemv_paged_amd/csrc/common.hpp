@@ -88,8 +88,8 @@ int gemv_grid_size(int32_t N, int32_t K, int32_t batch);
 
 struct AttnArgs {
   const void* q = nullptr;          // fp16 [B][nh][d]
-  const void* k_pool = nullptr;     // layer K base: [page][nkv][16][d]
-  const void* v_pool = nullptr;
+  const void* k_pool = nullptr;     // layer K base: [page][nkv][16 tokens][d]
+  const void* v_pool = nullptr;     // layer V base: [page][nkv][d][16 tokens]
   const int32_t* page_table = nullptr;
   int32_t max_pages = 0, num_pages = 0;
   const int32_t* lens = nullptr;    // [B]
@@ -97,10 +97,18 @@ struct AttnArgs {
   void* out = nullptr;              // fp16 [B][nh][d]
   float* part_o = nullptr;          // [B][nh][S][d]
   float* part_ml = nullptr;         // [B][nh][S][2]
-  int32_t batch = 1, n_heads = 0, n_kv = 0, head_dim = 0, splits = 1;
+  int32_t batch = 1, n_heads = 0, n_kv = 0, head_dim = 0;
+  int32_t splits = 1, per = 8;      // from attn_plan(batch, n_kv, max_pages)
   int32_t* err = nullptr;
 };
-int attn_splits_for(int32_t max_pages);
+// Split of a sequence's pages over workgroups: S splits of ``per`` pages each.
+struct AttnPlan {
+  int32_t S = 1, per = 8;
+};
+AttnPlan attn_plan(int32_t batch, int32_t n_kv, int32_t max_pages);
+// Largest page-table width the attention kernels cover (64 splits x 8 waves x
+// 64 pages per wave = 32768 pages, 524288 tokens).
+constexpr int32_t kAttnMaxPages = 64 * 8 * 64;
 size_t attn_partial_bytes(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t splits);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

@@ -9,10 +9,12 @@
 //   group scale applied to the fp32 partial sums, and fused epilogues (bias +
 //   RoPE + KV-page append, residual add, SwiGLU, fp32 logits + argmax partials).
 // * Split-K paged decode attention ("What it actually builds": 16-token pages;
-//   daily.dev FAQ on the barrier inside a warp-id branch): each wave stages its
-//   own K/V pages in its own LDS slice and synchronises only itself; the single
-//   block-wide barrier sits in uniform control flow after the page loop, so
-//   partial tail pages are masked by position, never by a divergent barrier.
+//   daily.dev FAQ on the barrier inside a warp-id branch): scores and P.V on
+//   the matrix cores with the GQA query heads as the MFMA columns, K and V
+//   pages read straight into operand registers, one online softmax per lane;
+//   the single block-wide barrier sits in uniform control flow after the page
+//   loop, so partial tail pages are masked by position, never by a divergent
+//   barrier.
 // * Small kernels: embedding gather, KV append, argmax finalize, device unpack.
 #include <algorithm>
 
@@ -429,8 +431,13 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
         if (page < 0 || page >= p.num_pages) {
           raise_flag(p.err, 1);
         } else {
-          half_t* base = is_k ? p.kv_k : p.kv_v;
-          base[((static_cast<int64_t>(page) * p.n_kv + kvh) * kPageTokens + ps % kPageTokens) * d + i2] = outv;
+          const int64_t blk = (static_cast<int64_t>(page) * p.n_kv + kvh) * kPageTokens * d;
+          const int slot = ps % kPageTokens;
+          if (is_k) {
+            p.kv_k[blk + slot * d + i2] = outv;              // token-major
+          } else {
+            p.kv_v[blk + i2 * kPageTokens + slot] = outv;    // dim-major
+          }
         }
       }
     }
@@ -582,32 +589,53 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
 
 // ============================================================== attention
 //
-// Split-K paged decode attention. Workgroup (s, kv head, sequence) covers a
-// contiguous page range of the sequence; its kAttnWaves waves take pages
-// w, w+kAttnWaves, ... and each keeps one page in flight ahead of the one it
-// computes. A wave stages its page in its own LDS slice and synchronises only
-// itself; the block barrier sits in uniform control flow after the page loop,
-// and the tail page is masked by position. The query heads of a KV head share
-// every K/V load (GQA). When one workgroup covers the whole context it writes
-// the output; otherwise workgroups write (max, sum, output) partials and the
-// combine kernel merges them with the log-sum-exp rule.
+// Split-K paged decode attention on the matrix cores. Workgroup (split s, KV
+// head, sequence) covers pages [s*per, (s+1)*per) of the sequence; its
+// kAttnWaves waves take pages w, w + kAttnWaves, ... and each keeps the next
+// page's loads in flight while it computes the current one. The query heads
+// of a KV head (GQA) are the 16 columns of the MFMA tiles, so every K/V page
+// is loaded once for all of them:
+//   scores  S^T[t][h] = sum_d K[t][d] Q[h][d]    v_mfma_f32_16x16x32_f16, A = K page
+//                                                (token-major, as stored), B = Q^T
+//   output  O^T[d][h] += sum_t V^T[d][t] P^T[t][h]  v_mfma_f32_16x16x16_f16, A = V page
+//                                                (dim-major, as stored), B = the
+//                                                probabilities the lane just computed
+// so both operands come straight from HBM in register order, with no LDS
+// round trip. Each lane ends up owning one head (lane % 16) for the online
+// softmax, so the running max, sum and the rescale of O stay in the lane.
+// Tokens at or beyond the length are masked by position (scores to -inf, V
+// to 0), whatever the slot holds. The only block-wide barrier sits in uniform
+// control flow after the page loop ("How To Build Your Own LLM Runtime From
+// Scratch", FAQ on the barrier inside a warp-id branch). When one workgroup
+// covers the whole context it writes the output; otherwise workgroups write
+// (max, sum, output) partials and the combine kernel merges them with the
+// log-sum-exp rule.
+
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttnWaves = 8;
-constexpr int kMinPagesPerSplit = kAttnWaves;
 constexpr int kMaxSplits = 64;
+constexpr int kMaxPagesPerWave = 64;  // page ids held one per lane
+static_assert(kAttnMaxPages == kMaxSplits * kAttnWaves * kMaxPagesPerWave, "attention page limit");
+constexpr int kAttnTargetGroups = 512;
 
-int attn_splits_for(int32_t max_pages) {
-  return std::max(1, std::min(kMaxSplits, (max_pages + kMinPagesPerSplit - 1) / kMinPagesPerSplit));
+AttnPlan attn_plan(int32_t batch, int32_t n_kv, int32_t max_pages) {
+  AttnPlan p;
+  const int groups = std::max(1, batch * n_kv);
+  int S = std::max(1, (kAttnTargetGroups + groups - 1) / groups);
+  S = std::min(S, std::max(1, (max_pages + kAttnWaves - 1) / kAttnWaves));  // >= one page per wave
+  S = std::min(S, kMaxSplits);
+  int per = (max_pages + S - 1) / S;
+  per = std::max(per, (max_pages + kMaxSplits - 1) / kMaxSplits);
+  per = (per + kAttnWaves - 1) / kAttnWaves * kAttnWaves;
+  per = std::min(std::max(per, kAttnWaves), kAttnWaves * kMaxPagesPerWave);
+  p.per = per;
+  p.S = std::max(1, (max_pages + per - 1) / per);
+  return p;
 }
 
 size_t attn_partial_bytes(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t splits) {
   return static_cast<size_t>(batch) * n_heads * splits * (head_dim + 2) * sizeof(float);
-}
-
-__device__ __forceinline__ void split_geometry(int len, int max_pages, int S, int& npages, int& per, int& nact) {
-  npages = min((len + kPageTokens - 1) / kPageTokens, max_pages);
-  per = max(kMinPagesPerSplit, (npages + S - 1) / S);
-  nact = (npages + per - 1) / per;
 }
 
 struct AttnParams {
@@ -621,182 +649,152 @@ struct AttnParams {
   half_t* out;
   float* po;
   float* pml;
-  int n_heads, n_kv, S;
+  int n_heads, n_kv, S, per;
   int32_t* err;
 };
 
 template <int D, int REP>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnParams a) {
-  constexpr int DC = D / 4;                 // dims per lane in the score phase
-  constexpr int DPL = D / 64;               // dims per lane in the PV phase
-  constexpr int U4 = 16 * D * 2 / 16 / 64;  // uint4 per lane per page (K or V)
+  static_assert((D == 64 || D == 128) && REP >= 1 && REP <= 16, "unsupported head shape");
   constexpr int NW = kAttnWaves;
-  __shared__ __align__(16) half_t lk[NW][16 * D];
-  __shared__ __align__(16) half_t lv[NW][16 * D];
-  __shared__ float lp[NW][REP][16];
-  __shared__ float red_m[NW][REP], red_l[NW][REP];
-  __shared__ float red_o[NW][REP][D];
+  constexpr int KJ = D / 32;  // score MFMAs per page
+  constexpr int VC = D / 16;  // P.V MFMAs per page
+  constexpr int DP = D + 4;   // padded LDS row (bank spread across heads)
+  __shared__ float red_m[NW][16], red_l[NW][16];
+  __shared__ __align__(16) float red_o[NW][REP][DP];
 
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int t = lane >> 2, c = lane & 3;
-  const int len = a.lens[b] + a.len_add;
-  int npages, per, nact;
-  split_geometry(len, a.max_pages, a.S, npages, per, nact);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int p0 = s * a.per;
+  const int pend = min(a.max_pages, p0 + a.per);
+  // Q^T fragments: lane holds head r16, dims 32j + 8*g4 .. +7 (zero for the
+  // padding heads r16 >= REP, which load head 0 and discard it)
+  half8 qf[KJ];
+  {
+    const half_t* qh =
+        a.q + (static_cast<int64_t>(b) * a.n_heads + kvh * REP + (r16 < REP ? r16 : 0)) * D + 8 * g4;
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) qf[j] = *reinterpret_cast<const half8*>(qh + 32 * j);
+  }
+  // this wave's page ids, one per lane; they do not depend on the length, so
+  // these loads overlap with the length load
+  int pid = -1;
+  {
+    const int myp = p0 + w + lane * NW;
+    if (lane < kMaxPagesPerWave && myp < pend) pid = a.pt[static_cast<int64_t>(b) * a.max_pages + myp];
+  }
+  const int len = __builtin_amdgcn_readfirstlane(a.lens[b] + a.len_add);
+  const int npages = min((len + kPageTokens - 1) / kPageTokens, a.max_pages);
+  const int nact = (npages + a.per - 1) / a.per;
   if (s == 0 && tid == 0 && len > a.max_pages * kPageTokens) raise_flag(a.err, 2);
-  const int p0 = s * per, p1 = min(npages, p0 + per);
-  if (len <= 0 || p0 >= p1) {
+  if (len <= 0 || p0 >= npages) {
     if (len <= 0 && s == 0) {  // empty context: zero output
       for (int i = tid; i < REP * D; i += 64 * NW)
         a.out[(static_cast<int64_t>(b) * a.n_heads + kvh * REP + i / D) * D + i % D] = static_cast<half_t>(0.0f);
     }
     return;  // block-uniform
   }
+  const int p1 = min(npages, pend);
+  const int nmine = p0 + w < p1 ? (p1 - p0 - w + NW - 1) / NW : 0;  // wave-uniform
 
-  const float scale = 1.0f / sqrtf(static_cast<float>(D));
-  h2 qr[REP][DC / 2];
+  if (r16 >= REP) {
 #pragma unroll
-  for (int h = 0; h < REP; ++h) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(
-        a.q + (static_cast<int64_t>(b) * a.n_heads + kvh * REP + h) * D + c * DC);
+    for (int j = 0; j < KJ; ++j)
 #pragma unroll
-    for (int j = 0; j < DC / 8; ++j) {
-      const u32x4 v = src[j];
-      qr[h][4 * j + 0] = as_h2(v[0]);
-      qr[h][4 * j + 1] = as_h2(v[1]);
-      qr[h][4 * j + 2] = as_h2(v[2]);
-      qr[h][4 * j + 3] = as_h2(v[3]);
-    }
+      for (int e = 0; e < 8; ++e) qf[j][e] = static_cast<half_t>(0.0f);
   }
-  float m[REP], l[REP], o[REP][DPL];
-#pragma unroll
-  for (int h = 0; h < REP; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[h][e] = 0.0f;
-  }
+  const float qscale = 1.4426950408889634f / sqrtf(static_cast<float>(D));  // log2(e) / sqrt(d)
 
-  // page pg of this wave: physical id and its K/V rows, one page ahead
-  auto page_id = [&](int pg) -> int {
-    const int id = a.pt[static_cast<int64_t>(b) * a.max_pages + pg];
-    return (id >= 0 && id < a.num_pages) ? id : -1;
+  f4 o[VC];
+#pragma unroll
+  for (int c = 0; c < VC; ++c) o[c] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY, l = 0.0f;
+
+  // page k of this wave: K rows t = r16 (dims 32j + 8*g4 ..), V^T rows d = 16c + r16
+  // (tokens 4*g4 .. +3). An id outside the pool reads page 0 and is skipped.
+  auto load = [&](int k, half8 (&kf)[KJ], half4 (&vf)[VC]) {
+    const int id = __builtin_amdgcn_readlane(pid, k);
+    const int idc = (id >= 0 && id < a.num_pages) ? id : 0;
+    const int64_t base = (static_cast<int64_t>(idc) * a.n_kv + kvh) * (kPageTokens * D);
+    const half_t* kb = a.kp + base + r16 * D + 8 * g4;
+    const half_t* vb = a.vp + base + r16 * kPageTokens + 4 * g4;
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) kf[j] = *reinterpret_cast<const half8*>(kb + 32 * j);
+#pragma unroll
+    for (int c = 0; c < VC; ++c) vf[c] = *reinterpret_cast<const half4*>(vb + 16 * c * kPageTokens);
   };
-  u32x4 kreg[U4], vreg[U4];
-  int pg = p0 + w;
-  int cur = pg < p1 ? page_id(pg) : -1;
-  if (cur >= 0) {
-    const u32x4* ks = reinterpret_cast<const u32x4*>(a.kp + (static_cast<int64_t>(cur) * a.n_kv + kvh) * 16 * D);
-    const u32x4* vs = reinterpret_cast<const u32x4*>(a.vp + (static_cast<int64_t>(cur) * a.n_kv + kvh) * 16 * D);
+  // A page whose id is outside the pool counts as empty (and is reported after
+  // the loop), so the loop body stays free of branches around memory ops.
+  bool bad = false;
+  auto compute = [&](int k, const half8 (&kf)[KJ], half4 (&vf)[VC]) {
+    const int id = __builtin_amdgcn_readlane(pid, k);
+    const bool okp = id >= 0 && id < a.num_pages;
+    bad |= !okp;
+    const int valid = okp ? min(kPageTokens, len - (p0 + w + k * NW) * kPageTokens) : 0;
+    f4 sc = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < U4; ++i) {
-      kreg[i] = ks[i * 64 + lane];
-      vreg[i] = vs[i * 64 + lane];
+    for (int j = 0; j < KJ; ++j) sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[j], qf[j], sc, 0, 0, 0);
+    // lane holds S^T[t = 4*g4 + i][h = r16]
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = (4 * g4 + i < valid) ? sc[i] * qscale : -INFINITY;
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx);  // -inf only while every page so far was empty
+    const float alpha = mnew == -INFINITY ? 1.0f : exp2f(m - mnew);
+    half4 pf;
+    float ps = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pf[i] = static_cast<half_t>(sv[i] == -INFINITY ? 0.0f : exp2f(sv[i] - mnew));
+      ps += static_cast<float>(pf[i]);
+    }
+    l = l * alpha + ps;
+    m = mnew;
+    if (valid < kPageTokens) {  // tail page: unused slots may hold anything (NaN poison included)
+#pragma unroll
+      for (int c = 0; c < VC; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * g4 + i >= valid) vf[c][i] = static_cast<half_t>(0.0f);
+    }
+#pragma unroll
+    for (int c = 0; c < VC; ++c) {
+      o[c] *= alpha;
+      o[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf[c], pf, o[c], 0, 0, 0);
+    }
+  };
+
+  if (nmine > 0) {
+    half8 kA[KJ], kB[KJ];
+    half4 vA[VC], vB[VC];
+    load(0, kA, vA);
+    // the loads of page k+1 are issued before page k is computed; the last
+    // page is loaded again in place of a page past the end (uniform wait counts)
+    for (int k = 0; k < nmine; k += 2) {
+      load(min(k + 1, nmine - 1), kB, vB);
+      compute(k, kA, vA);
+      if (k + 1 >= nmine) break;
+      load(min(k + 2, nmine - 1), kA, vA);
+      compute(k + 1, kB, vB);
     }
   }
-  for (; pg < p1; pg += NW) {  // wave-uniform trip count, no block barrier inside
-    if (cur < 0) {
-      if (lane == 0) raise_flag(a.err, 2);
-    }
-    wave_sync();  // every lane is done with the previous page's LDS
-    if (cur >= 0) {
-#pragma unroll
-      for (int i = 0; i < U4; ++i) {
-        reinterpret_cast<u32x4*>(lk[w])[i * 64 + lane] = kreg[i];
-        reinterpret_cast<u32x4*>(lv[w])[i * 64 + lane] = vreg[i];
-      }
-    }
-    const int valid = cur >= 0 ? min(kPageTokens, len - pg * kPageTokens) : 0;
-    // issue the next page's loads before computing this one
-    const int nxt = pg + NW < p1 ? page_id(pg + NW) : -1;
-    if (nxt >= 0) {
-      const u32x4* ks = reinterpret_cast<const u32x4*>(a.kp + (static_cast<int64_t>(nxt) * a.n_kv + kvh) * 16 * D);
-      const u32x4* vs = reinterpret_cast<const u32x4*>(a.vp + (static_cast<int64_t>(nxt) * a.n_kv + kvh) * 16 * D);
-#pragma unroll
-      for (int i = 0; i < U4; ++i) {
-        kreg[i] = ks[i * 64 + lane];
-        vreg[i] = vs[i * 64 + lane];
-      }
-    }
-    wave_sync();
-    if (valid > 0) {
-      // scores: lane (t, c) covers token t, dims [c*DC, c*DC + DC)
-      float sc[REP];
-      const u32x4* kr = reinterpret_cast<const u32x4*>(lk[w] + t * D + c * DC);
-#pragma unroll
-      for (int h = 0; h < REP; ++h) sc[h] = 0.0f;
-#pragma unroll
-      for (int j = 0; j < DC / 8; ++j) {
-        const u32x4 kk = kr[j];
-#pragma unroll
-        for (int h = 0; h < REP; ++h) {
-          sc[h] = dot2(qr[h][4 * j + 0], kk[0], sc[h]);
-          sc[h] = dot2(qr[h][4 * j + 1], kk[1], sc[h]);
-          sc[h] = dot2(qr[h][4 * j + 2], kk[2], sc[h]);
-          sc[h] = dot2(qr[h][4 * j + 3], kk[3], sc[h]);
-        }
-      }
-      float pr[REP];
-#pragma unroll
-      for (int h = 0; h < REP; ++h) {
-        float v = sc[h];
-        v += __shfl_xor(v, 1);
-        v += __shfl_xor(v, 2);
-        v = (t < valid) ? v * scale : -INFINITY;
-        float mx = v;
-        mx = fmaxf(mx, __shfl_xor(mx, 4));
-        mx = fmaxf(mx, __shfl_xor(mx, 8));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m[h], mx);
-        const float alpha = expf(m[h] - mnew);
-        pr[h] = expf(v - mnew);
-        l[h] = l[h] * alpha + (c == 0 ? pr[h] : 0.0f);
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) o[h][e] *= alpha;
-        m[h] = mnew;
-      }
-      if (c == 0) {
-#pragma unroll
-        for (int h = 0; h < REP; ++h) lp[w][h][t] = pr[h];
-      }
-      wave_sync();
-      // PV: lane owns dims [lane*DPL, lane*DPL + DPL)
-#pragma unroll 4
-      for (int t2 = 0; t2 < kPageTokens; ++t2) {
-        float vv[DPL];
-        if constexpr (DPL == 2) {
-          const h2 v2 = *reinterpret_cast<const h2*>(lv[w] + t2 * D + lane * 2);
-          vv[0] = static_cast<float>(v2[0]);
-          vv[DPL - 1] = static_cast<float>(v2[1]);
-        } else {
-          vv[0] = static_cast<float>(lv[w][t2 * D + lane]);
-        }
-        const bool ok = t2 < valid;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) vv[e] = ok ? vv[e] : 0.0f;
-#pragma unroll
-        for (int h = 0; h < REP; ++h) {
-          const float pv = lp[w][h][t2];
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) o[h][e] = fmaf(pv, vv[e], o[h][e]);
-        }
-      }
-    }
-    cur = nxt;
-  }
+
+  if (bad && lane == 0) raise_flag(a.err, 2);
 
   // combine the waves (uniform control flow: every wave reaches the barrier)
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (g4 == 0) {
+    red_m[w][r16] = m;
+    red_l[w][r16] = l;
+  }
+  if (r16 < REP) {
 #pragma unroll
-  for (int h = 0; h < REP; ++h) {
-    float v = l[h];
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    if (lane == 0) {
-      red_m[w][h] = m[h];
-      red_l[w][h] = v;
-    }
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) red_o[w][h][lane * DPL + e] = o[h][e];
+    for (int c = 0; c < VC; ++c) *reinterpret_cast<f4*>(&red_o[w][r16][16 * c + 4 * g4]) = o[c];
   }
   __syncthreads();
   const int64_t row0 = (static_cast<int64_t>(b) * a.n_heads + kvh * REP) * a.S;
@@ -808,7 +806,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnParams
     float L = 0.0f, O = 0.0f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
-      const float f = (red_m[ww][h] == -INFINITY) ? 0.0f : expf(red_m[ww][h] - M);
+      const float f = (red_m[ww][h] == -INFINITY) ? 0.0f : exp2f(red_m[ww][h] - M);
       L = fmaf(f, red_l[ww][h], L);
       O = fmaf(f, red_o[ww][h][d], O);
     }
@@ -825,15 +823,16 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnParams
   }
 }
 
-// grid (n_heads, B), D threads: merge the split partials of one query head.
+// grid (n_heads, B), D threads: merge the split partials of one query head
+// (maxima are in log2 units).
 template <int D>
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams a) {
   __shared__ float wgt[kMaxSplits];
   __shared__ float inv_l;
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int len = a.lens[b] + a.len_add;
-  int npages, per, nact;
-  split_geometry(len, a.max_pages, a.S, npages, per, nact);
+  const int npages = min((len + kPageTokens - 1) / kPageTokens, a.max_pages);
+  const int nact = (npages + a.per - 1) / a.per;
   if (len <= 0 || nact <= 1) return;  // the split kernel wrote the output
   const int64_t rb = (static_cast<int64_t>(b) * a.n_heads + h) * a.S;
   if (d < 64) {  // one wave: max and softmax weights of the splits
@@ -841,7 +840,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams a) {
     const float l0 = d < nact ? a.pml[(rb + d) * 2 + 1] : 0.0f;
     float M = m0;
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const float f = (m0 == -INFINITY) ? 0.0f : expf(m0 - M);
+    const float f = (m0 == -INFINITY) ? 0.0f : exp2f(m0 - M);
     float L = f * l0;
     for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
     if (d < nact) wgt[d] = f;
@@ -870,13 +869,14 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   p.n_heads = a.n_heads;
   p.n_kv = a.n_kv;
   p.S = a.splits;
+  p.per = a.per;
   p.err = a.err;
   const int rep = a.n_heads / a.n_kv;
   const dim3 grid(p.S, p.n_kv, a.batch), block(64 * kAttnWaves);
 #define NQ_ATT(DD, RR)                                                                   \
   if (a.head_dim == DD && rep == RR) {                                                   \
     attn_decode_kernel<DD, RR><<<grid, block, 0, s>>>(p);                                \
-    attn_combine_kernel<DD><<<dim3(a.n_heads, a.batch), dim3(DD), 0, s>>>(p);            \
+    if (p.S > 1) attn_combine_kernel<DD><<<dim3(a.n_heads, a.batch), dim3(DD), 0, s>>>(p); \
     return hipGetLastError();                                                            \
   }
   NQ_ATT(128, 7) NQ_ATT(128, 8) NQ_ATT(128, 4) NQ_ATT(128, 2) NQ_ATT(128, 1)
@@ -904,12 +904,16 @@ __global__ void kv_append_kernel(half_t* kp, half_t* vp, int n_kv, int d, const 
     return;
   }
   const int items = n_kv * d / 8;
+  const int slot = ps % kPageTokens;
   for (int i = threadIdx.x; i < items; i += blockDim.x) {
     const int h = (i * 8) / d, e = (i * 8) % d;
-    const int64_t dst = ((static_cast<int64_t>(page) * n_kv + h) * kPageTokens + ps % kPageTokens) * d + e;
+    const int64_t blk = (static_cast<int64_t>(page) * n_kv + h) * kPageTokens * d;
     const int64_t src = (static_cast<int64_t>(b) * n_kv + h) * d + e;
-    *reinterpret_cast<uint4*>(kp + dst) = *reinterpret_cast<const uint4*>(k + src);
-    *reinterpret_cast<uint4*>(vp + dst) = *reinterpret_cast<const uint4*>(v + src);
+    *reinterpret_cast<uint4*>(kp + blk + slot * d + e) = *reinterpret_cast<const uint4*>(k + src);  // token-major
+    const uint4 vv = *reinterpret_cast<const uint4*>(v + src);
+    const half_t* vh = reinterpret_cast<const half_t*>(&vv);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vp[blk + (e + j) * kPageTokens + slot] = vh[j];  // dim-major
   }
 }
 

@@ -52,7 +52,7 @@ struct Workspace {
   float* part_ml;
   float* amax_val;
   int32_t* amax_idx;
-  int splits;
+  AttnPlan attn;
   size_t total;
 };
 
@@ -65,14 +65,14 @@ Workspace carve(const nq_config& c, int32_t batch, int32_t max_pages, uint8_t* b
     return p;
   };
   const int32_t qd = c.n_heads * c.head_dim;
-  w.splits = attn_splits_for(max_pages);
+  w.attn = attn_plan(batch, c.n_kv_heads, max_pages);
   w.err = reinterpret_cast<int32_t*>(take(256));
   w.h = take(static_cast<size_t>(batch) * c.hidden * 2);
   w.qbuf = take(static_cast<size_t>(batch) * qd * 2);
   w.attn_o = take(static_cast<size_t>(batch) * qd * 2);
   w.act = take(static_cast<size_t>(batch) * c.intermediate * 2);
-  w.part_o = reinterpret_cast<float*>(take(static_cast<size_t>(batch) * c.n_heads * w.splits * c.head_dim * 4));
-  w.part_ml = reinterpret_cast<float*>(take(static_cast<size_t>(batch) * c.n_heads * w.splits * 2 * 4));
+  w.part_o = reinterpret_cast<float*>(take(static_cast<size_t>(batch) * c.n_heads * w.attn.S * c.head_dim * 4));
+  w.part_ml = reinterpret_cast<float*>(take(static_cast<size_t>(batch) * c.n_heads * w.attn.S * 2 * 4));
   const int64_t P = gemv_grid_size(c.vocab, c.hidden, batch);
   w.amax_val = reinterpret_cast<float*>(take(static_cast<size_t>(batch) * P * 4));
   w.amax_idx = reinterpret_cast<int32_t*>(take(static_cast<size_t>(batch) * P * 4));
@@ -89,6 +89,7 @@ nq_status check_io(const nq_model* m, const nq_step_io* io) {
   if (io->batch < 1 || io->batch > m->cfg.max_batch)
     return fail(NQ_ERR_INVALID_ARG, "batch %d outside 1..%d", io->batch, m->cfg.max_batch);
   if (io->max_pages < 1) return fail(NQ_ERR_INVALID_ARG, "max_pages must be >= 1");
+  if (io->max_pages > kAttnMaxPages) return fail(NQ_ERR_OUT_OF_RANGE, "max_pages %d > %d", io->max_pages, kAttnMaxPages);
   if (!io->page_table || !io->tokens || !io->pos)
     return fail(NQ_ERR_INVALID_ARG, "page_table, tokens and pos are required");
   if (io->token_hist && io->hist_len < 1) return fail(NQ_ERR_INVALID_ARG, "hist_len must be >= 1");
@@ -179,7 +180,8 @@ int enqueue_step(nq_model* m, nq_kv* kv, const nq_step_io* io, hipStream_t s) {
     at.n_heads = c.n_heads;
     at.n_kv = c.n_kv_heads;
     at.head_dim = c.head_dim;
-    at.splits = w.splits;
+    at.splits = w.attn.S;
+    at.per = w.attn.per;
     at.err = err;
     if ((e = launch_attention(at, s)) != hipSuccess) return hip_fail(e, "attention launch"), -1;
 
@@ -221,7 +223,7 @@ int enqueue_step(nq_model* m, nq_kv* kv, const nq_step_io* io, hipStream_t s) {
     dn.epi = NQ_EPI_RESIDUAL_F16;
     dn.err = err;
     if ((e = launch_gemv(dn, s)) != hipSuccess) return hip_fail(e, "down gemv launch"), -1;
-    launches += 6;
+    launches += w.attn.S > 1 ? 6 : 5;  // the combine kernel runs only when pages are split
   }
   GemvArgs lm{};
   lm.packed = m->lm;
@@ -337,8 +339,8 @@ nq_status nq_kv_append(nq_kv* kv, int32_t layer, int32_t batch, const int32_t* p
 }
 
 size_t nq_attn_workspace_bytes(const nq_config* cfg, int32_t batch, int32_t max_pages) {
-  if (nq_config_check(cfg) != NQ_OK || batch < 1 || max_pages < 1) return 0;
-  const int S = attn_splits_for(max_pages);
+  if (nq_config_check(cfg) != NQ_OK || batch < 1 || max_pages < 1 || max_pages > kAttnMaxPages) return 0;
+  const int S = attn_plan(batch, cfg->n_kv_heads, max_pages).S;
   return align256(static_cast<size_t>(batch) * cfg->n_heads * S * cfg->head_dim * 4) +
          align256(static_cast<size_t>(batch) * cfg->n_heads * S * 2 * 4);
 }
@@ -350,6 +352,7 @@ nq_status nq_attn_decode(const nq_kv* kv, int32_t layer, int32_t batch, const vo
   if (layer < 0 || layer >= kv->cfg.layers) return fail(NQ_ERR_OUT_OF_RANGE, "layer %d out of range", layer);
   if (batch < 1) return fail(NQ_ERR_INVALID_ARG, "batch must be >= 1");
   if (max_pages < 1) return fail(NQ_ERR_INVALID_ARG, "max_pages must be >= 1");
+  if (max_pages > kAttnMaxPages) return fail(NQ_ERR_OUT_OF_RANGE, "max_pages %d > %d", max_pages, kAttnMaxPages);
   if (!q || !page_table || !lens || !out || !workspace)
     return fail(NQ_ERR_INVALID_ARG, "null pointer");
   if (!aligned16(q) || !aligned16(workspace)) return fail(NQ_ERR_INVALID_ARG, "q and workspace must be 16-byte aligned");
@@ -371,7 +374,9 @@ nq_status nq_attn_decode(const nq_kv* kv, int32_t layer, int32_t batch, const vo
   a.n_heads = kv->cfg.n_heads;
   a.n_kv = kv->cfg.n_kv_heads;
   a.head_dim = kv->cfg.head_dim;
-  a.splits = attn_splits_for(max_pages);
+  const AttnPlan plan = attn_plan(batch, kv->cfg.n_kv_heads, max_pages);
+  a.splits = plan.S;
+  a.per = plan.per;
   a.part_o = static_cast<float*>(workspace);
   const size_t o_bytes = align256(static_cast<size_t>(batch) * a.n_heads * a.splits * a.head_dim * 4);
   a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + o_bytes);
@@ -424,7 +429,9 @@ nq_status nq_model_bind_rope(nq_model* m, const void* rope) {
 }
 
 size_t nq_workspace_bytes(const nq_config* cfg, int32_t batch, int32_t max_pages) {
-  if (nq_config_check(cfg) != NQ_OK || batch < 1 || batch > cfg->max_batch || max_pages < 1) return 0;
+  if (nq_config_check(cfg) != NQ_OK || batch < 1 || batch > cfg->max_batch || max_pages < 1 ||
+      max_pages > kAttnMaxPages)
+    return 0;
   return carve(*cfg, batch, max_pages, nullptr).total;
 }
 

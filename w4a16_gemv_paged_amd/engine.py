@@ -93,8 +93,9 @@ class KVCache:
         self.handle = nq_kv_alloc(model.cfg, self.pool, nbytes, num_pages)
 
     def view(self, cfg: NQConfig) -> torch.Tensor:
-        """The pool as fp16 [layer][2][page][kv_head][16][head_dim] (bit view)."""
-        return self.pool.view(torch.float16).view(cfg.layers, 2, self.num_pages, cfg.n_kv_heads, 16, cfg.head_dim)
+        """The pool as fp16 [layer][2][page][kv_head][16 * head_dim] (bit view); K pages
+        are token-major ([16][head_dim]) and V pages dim-major ([head_dim][16])."""
+        return self.pool.view(torch.float16).view(cfg.layers, 2, self.num_pages, cfg.n_kv_heads, 16 * cfg.head_dim)
 
     def close(self):
         if self.handle:

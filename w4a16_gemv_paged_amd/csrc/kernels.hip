@@ -205,6 +205,19 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
     }
   }
 
+  // The residual the epilogue adds to does not depend on the GEMV either.
+  float e_res = 0.0f;
+  if constexpr (EPI == NQ_EPI_RESIDUAL_F16) {
+    if (tid < items) {
+      const int tl2 = tid / (B * 16), b = (tid / 16) % B, rr = tid & 15;
+      const int64_t tt = static_cast<int64_t>(blockIdx.x) * p.tpw + tl2;
+      if (tt < p.T) {
+        const int64_t n = tile_row_logical(p.kind, p.N, p.head_dim, tt, rr);
+        if (n < p.N) e_res = static_cast<float>(static_cast<const half_t*>(p.y)[b * static_cast<int64_t>(p.N) + n]);
+      }
+    }
+  }
+
   // Buffer descriptors over this tile's codes and scales: the per-group offset
   // is a scalar, the per-lane offset a constant; reads past the tile give 0.
   const int tq = tile_ok ? t : 0;
@@ -377,7 +390,8 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
     } else if constexpr (EPI == NQ_EPI_RESIDUAL_F16) {
       if (n < N) {
         half_t* yo = static_cast<half_t*>(p.y) + b * N + n;
-        const half_t v = static_cast<half_t>(static_cast<float>(*yo) + yv);
+        const float r = i == tid ? e_res : static_cast<float>(*yo);  // prefetched for item tid
+        const half_t v = static_cast<half_t>(r + yv);
         *yo = v;
         if (p.y2) p.y2[b * N + n] = v;
       }
@@ -481,17 +495,25 @@ struct GemvShape {
   size_t lds;
 };
 
-// Each wave owns at most kDepth groups of a tile where possible, so that all
-// of its weight loads are in flight at once; small-N matrices are split
-// further along K (at least 4 groups per slice) so that about 2048 waves share
-// the work; a workgroup has at least 4 waves. The staged activations (plus the
-// gain) get at most kLdsX bytes; longer K is processed in chunks.
+// Launch shape, from a sweep of (tiles per workgroup, K-slices) on MI355X at
+// the decode shapes. Matrices with few tiles (T < 1024: the QKV, O and down
+// projections) split K so that each wave owns about 7 groups (at most 8
+// slices) and run one tile per workgroup below 256 tiles, two above. Matrices
+// with many tiles (gate/up, LM head) already fill the chip with workgroups:
+// two tiles x two K-slices at batch 1-3, eight tiles x one slice from batch 4,
+// where each loaded block feeds more matrix-core columns. The staged
+// activations (plus the gain) get at most kLdsX bytes; longer K is processed
+// in chunks.
 static GemvShape gemv_shape(int T, int G, int B, bool gain) {
   GemvShape s;
-  const int need = (G + kDepth - 1) / kDepth;
-  const int spread = std::min((2048 + T - 1) / T, std::max(1, G / 4));
-  s.ks = std::max(1, std::min(16, std::max(need, spread)));
-  s.tpw = std::max(1, std::min(16 / s.ks, 4 / s.ks > 0 ? 4 / s.ks : 1));
+  if (T >= 1024) {
+    s.ks = B >= 4 ? 1 : 2;
+    s.tpw = B >= 4 ? 8 : 2;
+  } else {
+    s.ks = std::min(8, (G + 6) / 7);
+    s.tpw = T >= 256 ? 2 : 1;
+  }
+  s.ks = std::max(1, std::min(s.ks, G));
   const int rows = B + (gain ? 1 : 0);
   const int fit = static_cast<int>(kLdsX / (static_cast<size_t>(rows) * 256)) / 4 * 4;  // whole 1 KiB blocks
   s.ch = G <= fit ? G : std::max(s.ks, fit / s.ks * s.ks);
@@ -687,14 +709,17 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnParams
   }
   const int len = __builtin_amdgcn_readfirstlane(a.lens[b] + a.len_add);
   const int npages = min((len + kPageTokens - 1) / kPageTokens, a.max_pages);
-  const int nact = (npages + a.per - 1) / a.per;
   if (s == 0 && tid == 0 && len > a.max_pages * kPageTokens) raise_flag(a.err, 2);
-  if (len <= 0 || p0 >= npages) {
-    if (len <= 0 && s == 0) {  // empty context: zero output
+  const int64_t row0 = (static_cast<int64_t>(b) * a.n_heads + kvh * REP) * a.S;
+  if (len <= 0 || p0 >= npages) {  // block-uniform
+    if (a.S == 1) {                // empty context: zero output
       for (int i = tid; i < REP * D; i += 64 * NW)
         a.out[(static_cast<int64_t>(b) * a.n_heads + kvh * REP + i / D) * D + i % D] = static_cast<half_t>(0.0f);
+    } else if (tid < REP) {        // an empty split: weight 0 in the combine
+      a.pml[(row0 + static_cast<int64_t>(tid) * a.S + s) * 2] = -INFINITY;
+      a.pml[(row0 + static_cast<int64_t>(tid) * a.S + s) * 2 + 1] = 0.0f;
     }
-    return;  // block-uniform
+    return;
   }
   const int p1 = min(npages, pend);
   const int nmine = p0 + w < p1 ? (p1 - p0 - w + NW - 1) / NW : 0;  // wave-uniform
@@ -797,7 +822,6 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnParams
     for (int c = 0; c < VC; ++c) *reinterpret_cast<f4*>(&red_o[w][r16][16 * c + 4 * g4]) = o[c];
   }
   __syncthreads();
-  const int64_t row0 = (static_cast<int64_t>(b) * a.n_heads + kvh * REP) * a.S;
   for (int i = tid; i < REP * D; i += 64 * NW) {
     const int h = i / D, d = i % D;
     float M = -INFINITY;
@@ -810,7 +834,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnParams
       L = fmaf(f, red_l[ww][h], L);
       O = fmaf(f, red_o[ww][h][d], O);
     }
-    if (nact == 1) {
+    if (a.S == 1) {
       a.out[(static_cast<int64_t>(b) * a.n_heads + kvh * REP + h) * D + d] = static_cast<half_t>(L > 0.0f ? O / L : 0.0f);
     } else {
       const int64_t row = row0 + static_cast<int64_t>(h) * a.S + s;
@@ -823,33 +847,39 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnParams
   }
 }
 
-// grid (n_heads, B), D threads: merge the split partials of one query head
-// (maxima are in log2 units).
+// grid (n_heads, B), D threads: merge the S split partials of one query head
+// (maxima in log2 units). Every split wrote its row (an empty one with max
+// -inf), so nothing here waits for the length: the partial loads go out at once.
 template <int D>
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams a) {
+  constexpr int kEarly = 8;  // partials per thread loaded before the weights are known
   __shared__ float wgt[kMaxSplits];
   __shared__ float inv_l;
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int len = a.lens[b] + a.len_add;
-  const int npages = min((len + kPageTokens - 1) / kPageTokens, a.max_pages);
-  const int nact = (npages + a.per - 1) / a.per;
-  if (len <= 0 || nact <= 1) return;  // the split kernel wrote the output
-  const int64_t rb = (static_cast<int64_t>(b) * a.n_heads + h) * a.S;
+  const int S = a.S;
+  const int64_t rb = (static_cast<int64_t>(b) * a.n_heads + h) * S;
+  float pv[kEarly];
+#pragma unroll
+  for (int s = 0; s < kEarly; ++s) pv[s] = s < S ? a.po[(rb + s) * D + d] : 0.0f;
   if (d < 64) {  // one wave: max and softmax weights of the splits
-    const float m0 = d < nact ? a.pml[(rb + d) * 2] : -INFINITY;
-    const float l0 = d < nact ? a.pml[(rb + d) * 2 + 1] : 0.0f;
+    const float m0 = d < S ? a.pml[(rb + d) * 2] : -INFINITY;
+    const float l0 = d < S ? a.pml[(rb + d) * 2 + 1] : 0.0f;
     float M = m0;
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     const float f = (m0 == -INFINITY) ? 0.0f : exp2f(m0 - M);
     float L = f * l0;
     for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-    if (d < nact) wgt[d] = f;
+    if (d < S) wgt[d] = f;
     if (d == 0) inv_l = L > 0.0f ? 1.0f / L : 0.0f;
   }
   __syncthreads();
+  // an empty split's output row was never written: its weight selects 0, not 0 * (stale value)
   float O = 0.0f;
-#pragma unroll 8
-  for (int s = 0; s < nact; ++s) O = fmaf(wgt[s], a.po[(rb + s) * D + d], O);
+#pragma unroll
+  for (int s = 0; s < kEarly; ++s)
+    if (s < S && wgt[s] != 0.0f) O = fmaf(wgt[s], pv[s], O);
+  for (int s = kEarly; s < S; ++s)
+    if (wgt[s] != 0.0f) O = fmaf(wgt[s], a.po[(rb + s) * D + d], O);
   a.out[(static_cast<int64_t>(b) * a.n_heads + h) * D + d] = static_cast<half_t>(O * inv_l);
 }
 

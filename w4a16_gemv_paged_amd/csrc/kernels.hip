@@ -490,6 +490,296 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
   }
 }
 
+// ---------------------------------------------------------------- streaming GEMV
+//
+// For matrices with very many tiles (at least 16 per workgroup: the LM head)
+// a fixed grid of kStreamGroups workgroups of kStreamWaves waves streams the
+// whole matrix: workgroup i owns the contiguous tiles
+// [T*i/kStreamGroups, T*(i+1)/kStreamGroups) and stages the activations (and
+// the gain) in LDS once. Its tiles are cut into chunks of at most
+// kStreamChunk consecutive groups; waves take chunks from an LDS counter as
+// they finish, so fast and slow waves end together, and each wave keeps two
+// chunks in flight (the next one is loaded before the current one is
+// computed). A chunk's partial sums go to the chunk's own LDS slot, and the
+// epilogue adds a tile's slots in chunk order, so the result does not depend
+// on which wave took which chunk.
+
+constexpr int kStreamGroups = 256;
+constexpr int kStreamWaves = 16;
+constexpr int kStreamChunk = 8;  // groups per chunk (ring slots per chunk buffer)
+
+struct StreamPlan {
+  bool ok = false;
+  int tiles_per_group = 0, chunks_per_tile = 0;
+  size_t lds = 0;
+  int xrow = 0;
+};
+
+static StreamPlan stream_plan(int T, int G, int B, bool gain) {
+  StreamPlan s;
+  s.tiles_per_group = (T + kStreamGroups - 1) / kStreamGroups;
+  s.chunks_per_tile = (G + kStreamChunk - 1) / kStreamChunk;
+  s.xrow = (G * 128 + 511) / 512 * 512;
+  const int rows = B + (gain ? 1 : 0);
+  const size_t xbytes = static_cast<size_t>(rows) * s.xrow * 2;
+  const size_t lg = static_cast<size_t>(s.tiles_per_group) * B * 16 * 4;  // argmax logits, reuse the x rows
+  s.lds = std::max(xbytes, lg) + 256 + 16 +
+          static_cast<size_t>(s.tiles_per_group) * s.chunks_per_tile * B * 16 * 4 +  // chunk partials
+          static_cast<size_t>(kStreamWaves) * B * 4;                                // sum of squares
+  // measured: the LM head gains (9504 tiles), gate/up (2368 tiles) is faster
+  // with one tile set per workgroup
+  s.ok = T >= 16 * kStreamGroups && s.lds <= 150 * 1024;
+  return s;
+}
+
+template <int B, int EPI, bool GAIN>
+__global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int NW = kStreamWaves;
+  constexpr int CH = kStreamChunk;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, kb = lane >> 4;
+  const int G = p.G, xrow = p.xrow, cpt = p.ks;  // ks carries the chunks per tile
+  const int t0 = static_cast<int>(static_cast<int64_t>(p.T) * blockIdx.x / gridDim.x);
+  const int t1 = static_cast<int>(static_cast<int64_t>(p.T) * (blockIdx.x + 1) / gridDim.x);
+  const int ntl = t1 - t0;                  // tiles of this workgroup (<= p.tpw)
+  const int nb = ntl * G;                   // their blocks, contiguous in memory
+  const int Q = ntl * cpt;                  // chunks
+  // LDS: [B] activation rows | gain row | zero block | counter | part | ssq
+  half_t* xs = reinterpret_cast<half_t*>(smem);
+  half_t* gs = xs + B * xrow;
+  const int xbytes = (B + (GAIN ? 1 : 0)) * xrow * 2;
+  const int lgbytes = p.tpw * B * 16 * 4;
+  half_t* zero = reinterpret_cast<half_t*>(smem + (xbytes > lgbytes ? xbytes : lgbytes));
+  int* next_chunk = reinterpret_cast<int*>(zero + 128);
+  float* part = reinterpret_cast<float*>(next_chunk + 4);  // [chunk][B][16]
+  float* ssq = part + p.tpw * cpt * B * 16;                  // [NW][B]
+  float* lg = reinterpret_cast<float*>(smem);                // [tile][B][16], after the stream
+  const uint32_t magic = opaque(0x64006400u);
+
+  // the residual the epilogue adds to: one prefetched item per thread
+  float e_res = 0.0f;
+  if constexpr (EPI == NQ_EPI_RESIDUAL_F16) {
+    if (tid < ntl * B * 16) {
+      const int j = tid / (B * 16), b = (tid / 16) % B, rr = tid & 15;
+      const int64_t n = tile_row_logical(p.kind, p.N, p.head_dim, t0 + j, rr);
+      if (n < p.N) e_res = static_cast<float>(static_cast<const half_t*>(p.y)[b * static_cast<int64_t>(p.N) + n]);
+    }
+  }
+
+  // descriptors over this workgroup's codes and scales (reads past the end give 0)
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.codes) + static_cast<size_t>(t0) * G * kBlockBytes, 0, nb * kBlockBytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.scales) + static_cast<size_t>(t0) * G * 32, 0, nb * 32, kBufferFlags);
+  const int wvoff = lane * 16, svoff = kb * 8;
+  const half_t* xlane = (col < B ? xs + col * xrow : zero) + kb * 32;
+  const int xstep = col < B ? 128 : 0;
+  if (tid < 16) reinterpret_cast<uint4*>(zero)[tid] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid == 0) *next_chunk = 2 * NW;       // chunks w and NW + w start on wave w
+
+  // (1) activations and gain into LDS, issued before the weights
+  {
+    const int n8 = G * 16;                  // 16-byte items per row
+    const int rblk = (n8 + 63) / 64;        // 1 KiB blocks per row
+    const int nblk = (B + (GAIN ? 1 : 0)) * rblk;
+    const int mine = (nblk - wave + NW - 1) / NW;
+    for (int r0 = 0; r0 < mine; r0 += kDmaBatch) {
+#pragma unroll
+      for (int q = 0; q < kDmaBatch; ++q) {
+        const int bi = wave + (r0 + q) * NW;
+        if (r0 + q < mine) {
+          const int r = bi / rblk, j = bi - r * rblk;
+          const int item = j * 64 + lane;
+          const half_t* src = r < B ? p.x + static_cast<int64_t>(r) * p.K + item * 8 : p.gain + item * 8;
+          half_t* dst = r < B ? xs + r * xrow + j * 512 : gs + j * 512;
+          if (item < n8) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // chunk q = (tile q / cpt, groups [c*G/cpt, (c+1)*G/cpt) with c = q % cpt);
+  // slot s of a chunk buffer holds the chunk's group g0 + s, or zeros
+  auto chunk_range = [&](int q, int& g0, int& g1, int& j) {
+    j = q / cpt;
+    const int c = q - j * cpt;
+    g0 = c * G / cpt;
+    g1 = (c + 1) * G / cpt;
+  };
+  auto load_chunk = [&](int q, u32x4 (&w)[CH], u32x2 (&sc)[CH]) {
+    int g0, g1, j;
+    chunk_range(q, g0, g1, j);
+    const bool in = q < Q;
+#pragma unroll
+    for (int s2 = 0; s2 < CH; ++s2) {
+      const int f = (in && g0 + s2 < g1) ? j * G + g0 + s2 : nb;   // nb: out of range, reads 0
+      w[s2] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff, f * kBlockBytes, 0);
+      sc[s2] = __builtin_amdgcn_raw_buffer_load_b64(srs, svoff, f * 32, 0);
+    }
+  };
+  auto compute_chunk = [&](int q, const u32x4 (&w)[CH], const u32x2 (&sc)[CH]) {
+    int g0, g1, j;
+    chunk_range(q, g0, g1, j);
+    f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s2 = 0; s2 < CH; ++s2) {
+      const int g = min(g0 + s2, g1 - 1);  // a zero slot reads a valid activation group
+      const f4 d = gemv_block_mfma(w[s2], xlane + g * xstep, magic);
+      scale_acc(acc, d, sc[s2]);
+    }
+    if (col < B) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[(q * B + col) * 16 + 4 * kb + i] = acc[i];
+    }
+  };
+  auto grab = [&]() -> int {
+    int q = 0;
+    if (lane == 0) q = atomicAdd(next_chunk, 1);
+    return __builtin_amdgcn_readfirstlane(q);
+  };
+
+  // (2) The activations land before any weight is requested. Every workgroup
+  //     reads the same few KiB at the same moment; behind a flood of weight
+  //     requests those lines would wait for several microseconds, in front of
+  //     it they cost one memory round trip. Then the first two chunks of each
+  //     wave are requested.
+  __builtin_amdgcn_s_waitcnt(0);     // activation copies and the chunk counter
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 wa[CH], wb[CH];
+  u32x2 sa[CH], sb[CH];
+  int qa = wave;
+  int qb = NW + wave;
+  load_chunk(qa, wa, sa);
+  load_chunk(qb, wb, sb);
+  __builtin_amdgcn_sched_barrier(0);
+  // (3) x * gain in place, and each wave's share of sum(x^2) per batch row
+  if constexpr (GAIN) {
+    const int n8 = G * 16;
+    for (int b = 0; b < B; ++b) {
+      float sacc = 0.0f;
+      for (int j = tid; j < n8; j += blockDim.x) {
+        uint4 v = *reinterpret_cast<const uint4*>(xs + b * xrow + j * 8);
+        const uint4 gv = *reinterpret_cast<const uint4*>(gs + j * 8);
+        half_t* hv = reinterpret_cast<half_t*>(&v);
+        const half_t* gh = reinterpret_cast<const half_t*>(&gv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = static_cast<float>(hv[e]);
+          sacc = fmaf(f, f, sacc);
+          hv[e] = static_cast<half_t>(f * static_cast<float>(gh[e]));
+        }
+        *reinterpret_cast<uint4*>(xs + b * xrow + j * 8) = v;
+      }
+      for (int o = 32; o >= 1; o >>= 1) sacc += __shfl_xor(sacc, o);
+      if (lane == 0) ssq[wave * B + b] = sacc;
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // (4) stream: compute the older chunk while the newer one is in flight, then
+  // refill its buffer with a freshly taken chunk. Chunk numbers only grow, so
+  // the first one past the end means every later one is too.
+  for (;;) {
+    if (qa >= Q) break;
+    compute_chunk(qa, wa, sa);
+    qa = grab();
+    load_chunk(qa, wa, sa);
+    if (qb >= Q) break;
+    compute_chunk(qb, wb, sb);
+    qb = grab();
+    load_chunk(qb, wb, sb);
+  }
+  __syncthreads();
+
+  // (5) epilogue over (tile, batch row, tile row) items
+  const int items = ntl * B * 16;
+  for (int i = tid; i < items; i += blockDim.x) {
+    const int j = i / (B * 16), b = (i / 16) % B, rr = i & 15;
+    const int64_t tt = t0 + j;
+    float yv = 0.0f, yp = 0.0f;
+    for (int c = 0; c < cpt; ++c) {
+      yv += part[((j * cpt + c) * B + b) * 16 + rr];
+      yp += part[((j * cpt + c) * B + b) * 16 + (rr ^ 8)];
+    }
+    float rs = 1.0f;
+    if constexpr (GAIN) {
+      float v = 0.0f;
+      for (int w = 0; w < NW; ++w) v += ssq[w * B + b];
+      rs = 1.0f / sqrtf(v / static_cast<float>(p.K) + p.eps);
+    }
+    yv *= rs;
+    yp *= rs;
+    const int64_t n = tile_row_logical(p.kind, p.N, p.head_dim, tt, rr);
+    const int64_t N = p.N;
+    if constexpr (EPI == NQ_EPI_STORE_F16) {
+      if (n < N) static_cast<half_t*>(p.y)[b * N + n] = static_cast<half_t>(yv);
+    } else if constexpr (EPI == NQ_EPI_BIAS_F16) {
+      if (n < N) static_cast<half_t*>(p.y)[b * N + n] = static_cast<half_t>(yv + static_cast<float>(p.bias[n]));
+    } else if constexpr (EPI == NQ_EPI_RESIDUAL_F16) {
+      if (n < N) {
+        half_t* yo = static_cast<half_t*>(p.y) + b * N + n;
+        const float r = i == tid ? e_res : static_cast<float>(*yo);
+        const half_t v = static_cast<half_t>(r + yv);
+        *yo = v;
+        if (p.y2) p.y2[b * N + n] = v;
+      }
+    } else if constexpr (EPI == NQ_EPI_SWIGLU_F16) {
+      if (rr < 8) {
+        const int64_t I = N / 2;
+        const float a = yv / (1.0f + expf(-yv)) * yp;
+        static_cast<half_t*>(p.y)[b * I + 8 * tt + rr] = static_cast<half_t>(a);
+      }
+    } else if constexpr (EPI == NQ_EPI_STORE_F32) {
+      if (n < N && p.y) static_cast<float*>(p.y)[b * N + n] = yv;
+      lg[(j * B + b) * 16 + rr] = (n < N) ? yv : -INFINITY;
+    }
+  }
+
+  if constexpr (EPI == NQ_EPI_STORE_F32) {
+    if (p.amax_val) {
+      __syncthreads();
+      // this workgroup's best (value, index) per batch row: wave b scans its row
+      if (wave < B) {
+        const int b = wave;
+        float best = -INFINITY;
+        int bi = 0x7fffffff;
+        bool nan = false;
+        for (int i = lane; i < ntl * 16; i += 64) {
+          const int j = i / 16, rr = i & 15;
+          const float v = lg[(j * B + b) * 16 + rr];
+          const int n = static_cast<int>(tile_row_logical(p.kind, p.N, p.head_dim, t0 + j, rr));
+          if (v != v) {
+            nan = true;
+          } else if (n < p.N && better(v, n, best, bi)) {
+            best = v;
+            bi = n;
+          }
+        }
+        for (int o = 32; o >= 1; o >>= 1) {
+          const float ov = __shfl_xor(best, o);
+          const int oi = __shfl_xor(bi, o);
+          if (better(ov, oi, best, bi)) {
+            best = ov;
+            bi = oi;
+          }
+        }
+        nan = __any(nan);
+        if (lane == 0) {
+          if (nan) raise_flag(p.err, 8);
+          p.amax_val[static_cast<int64_t>(b) * gridDim.x + blockIdx.x] = best;
+          p.amax_idx[static_cast<int64_t>(b) * gridDim.x + blockIdx.x] = bi;
+        }
+      }
+    }
+  }
+}
+
 struct GemvShape {
   int tpw, ks, ch, xrow, threads;
   size_t lds;
@@ -527,8 +817,60 @@ static GemvShape gemv_shape(int T, int G, int B, bool gain) {
 
 int gemv_grid_size(int32_t N, int32_t K, int32_t batch) {
   const int T = static_cast<int>(tiles_of(N));
+  if (stream_plan(T, K / kGroup, batch, true).ok) return kStreamGroups;
   const GemvShape sh = gemv_shape(T, K / kGroup, batch, true);
   return (T + sh.tpw - 1) / sh.tpw;
+}
+
+// Lets a streaming kernel take more than the default 64 KiB of dynamic LDS (once per kernel).
+template <int B, int EPI, bool GAIN>
+static hipError_t allow_stream_lds() {
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_stream_kernel<B, EPI, GAIN>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
+  return e;
+}
+
+template <int B, bool GAIN>
+static hipError_t launch_stream_e(int epi, size_t lds, hipStream_t stream, const GemvParams& p) {
+  const dim3 grid(kStreamGroups), block(64 * kStreamWaves);
+  hipError_t e = hipSuccess;
+  switch (epi) {
+    case NQ_EPI_STORE_F16: e = allow_stream_lds<B, NQ_EPI_STORE_F16, GAIN>(); break;
+    case NQ_EPI_BIAS_F16: e = allow_stream_lds<B, NQ_EPI_BIAS_F16, GAIN>(); break;
+    case NQ_EPI_RESIDUAL_F16: e = allow_stream_lds<B, NQ_EPI_RESIDUAL_F16, GAIN>(); break;
+    case NQ_EPI_SWIGLU_F16: e = allow_stream_lds<B, NQ_EPI_SWIGLU_F16, GAIN>(); break;
+    case NQ_EPI_STORE_F32: e = allow_stream_lds<B, NQ_EPI_STORE_F32, GAIN>(); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  switch (epi) {
+    case NQ_EPI_STORE_F16: gemv_stream_kernel<B, NQ_EPI_STORE_F16, GAIN><<<grid, block, lds, stream>>>(p); break;
+    case NQ_EPI_BIAS_F16: gemv_stream_kernel<B, NQ_EPI_BIAS_F16, GAIN><<<grid, block, lds, stream>>>(p); break;
+    case NQ_EPI_RESIDUAL_F16: gemv_stream_kernel<B, NQ_EPI_RESIDUAL_F16, GAIN><<<grid, block, lds, stream>>>(p); break;
+    case NQ_EPI_SWIGLU_F16: gemv_stream_kernel<B, NQ_EPI_SWIGLU_F16, GAIN><<<grid, block, lds, stream>>>(p); break;
+    case NQ_EPI_STORE_F32: gemv_stream_kernel<B, NQ_EPI_STORE_F32, GAIN><<<grid, block, lds, stream>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int B>
+static hipError_t launch_stream_g(bool gain, int epi, size_t lds, hipStream_t stream, const GemvParams& p) {
+  return gain ? launch_stream_e<B, true>(epi, lds, stream, p) : launch_stream_e<B, false>(epi, lds, stream, p);
+}
+
+static hipError_t launch_stream_b(int batch, bool gain, int epi, size_t lds, hipStream_t stream, const GemvParams& p) {
+  switch (batch) {
+    case 1: return launch_stream_g<1>(gain, epi, lds, stream, p);
+    case 2: return launch_stream_g<2>(gain, epi, lds, stream, p);
+    case 3: return launch_stream_g<3>(gain, epi, lds, stream, p);
+    case 4: return launch_stream_g<4>(gain, epi, lds, stream, p);
+    case 5: return launch_stream_g<5>(gain, epi, lds, stream, p);
+    case 6: return launch_stream_g<6>(gain, epi, lds, stream, p);
+    case 7: return launch_stream_g<7>(gain, epi, lds, stream, p);
+    case 8: return launch_stream_g<8>(gain, epi, lds, stream, p);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int B, bool GAIN>
@@ -605,6 +947,13 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
   p.rope = a.rope;
   p.max_pos = a.max_pos;
   p.err = a.err;
+  const StreamPlan sp = stream_plan(p.T, p.G, a.batch, a.norm_gain != nullptr);
+  if (sp.ok && a.epi != EPI_QKV_ROPE_KV && !a.embed) {
+    p.tpw = sp.tiles_per_group;  // the streaming kernel reads tpw / ks as tiles per group / chunks per tile
+    p.ks = sp.chunks_per_tile;
+    p.xrow = sp.xrow;
+    return launch_stream_b(a.batch, a.norm_gain != nullptr, a.epi, sp.lds, stream, p);
+  }
   const dim3 grid((p.T + p.tpw - 1) / p.tpw), block(sh.threads);
   return launch_gemv_b(a.batch, a.norm_gain != nullptr, a.epi, grid, block, sh.lds, stream, p);
 }

@@ -175,3 +175,44 @@ def test_batch8_logits_against_oracle(tiny):
             assert rel_inf(gpu["logits"][s, b], orc["logits"][i]) < TOL_LOGITS
         ok = orc["margins"] > MARGIN
         np.testing.assert_array_equal(gpu["tokens"][b][ok], orc["tokens"][ok])
+
+
+def test_split_attention_long_context(tiny):
+    """Batch 1 over 64-page tables: attention splits the pages over 8
+    workgroups whose partials the combine kernel merges. 200-token prompt
+    (13 pages at the end: two splits hold pages, the rest are empty). Logits and
+    tokens against the oracle; graph replay equals eager bitwise."""
+    om, dm = tiny
+    prompt = synth.prompt_ids(200, SHAPE.vocab, seed=60)
+    say("tiny long-context eager run")
+    gpu = _run(dm, [prompt], 8, pages=64, layers=False)
+    orc = oracle.generate(om, prompt, 8, forced=gpu["tokens"][0])
+    gl = gpu["logits"][len(prompt) - 1:, 0]
+    errs = [rel_inf(gl[i], orc["logits"][i]) for i in range(8)]
+    assert max(errs) < TOL_LOGITS, max(errs)
+    ok = orc["margins"] > MARGIN
+    np.testing.assert_array_equal(gpu["tokens"][0][ok], orc["tokens"][ok])
+    say("tiny long-context graph run")
+    g = _run(dm, [prompt], 8, pages=64, graph=True, layers=False)
+    np.testing.assert_array_equal(g["logits"].view(np.uint32), gpu["logits"].view(np.uint32))
+    assert g["kernels"] == 6 * SHAPE.layers + 2
+
+
+def test_split_attention_batch8(tiny):
+    """Batch 8 over 64-page tables: ragged prompts of 90-300 tokens span one to
+    three splits of the pages."""
+    om, dm = tiny
+    lens = (90, 300, 130, 210, 160, 250, 100, 180)
+    prompts = [synth.prompt_ids(n, SHAPE.vocab, seed=70 + i) for i, n in enumerate(lens)]
+    say("tiny long-context batch-8 run")
+    gpu = _run(dm, prompts, 3, pages=64, layers=False)
+    for b, p in enumerate(prompts):
+        orc = oracle.generate(om, p, 3, forced=gpu["tokens"][b])
+        for i, s in enumerate(range(len(p) - 1, len(p) + 2)):
+            assert rel_inf(gpu["logits"][s, b], orc["logits"][i]) < TOL_LOGITS, (b, i)
+        ok = orc["margins"] > MARGIN
+        np.testing.assert_array_equal(gpu["tokens"][b][ok], orc["tokens"][ok])
+    say("tiny long-context batch-8 graph run")
+    g = _run(dm, prompts, 3, pages=64, graph=True, layers=False)
+    assert g["kernels"] == 6 * SHAPE.layers + 2
+    np.testing.assert_array_equal(g["logits"].view(np.uint32), gpu["logits"].view(np.uint32))

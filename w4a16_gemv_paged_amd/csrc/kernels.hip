@@ -206,14 +206,14 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
   }
 
   // The residual the epilogue adds to does not depend on the GEMV either.
-  float e_res = 0.0f;
+  half_t e_res = static_cast<half_t>(0.0f);  // kept as loaded: converting it here would wait for it
   if constexpr (EPI == NQ_EPI_RESIDUAL_F16) {
     if (tid < items) {
       const int tl2 = tid / (B * 16), b = (tid / 16) % B, rr = tid & 15;
       const int64_t tt = static_cast<int64_t>(blockIdx.x) * p.tpw + tl2;
       if (tt < p.T) {
         const int64_t n = tile_row_logical(p.kind, p.N, p.head_dim, tt, rr);
-        if (n < p.N) e_res = static_cast<float>(static_cast<const half_t*>(p.y)[b * static_cast<int64_t>(p.N) + n]);
+        if (n < p.N) e_res = static_cast<const half_t*>(p.y)[b * static_cast<int64_t>(p.N) + n];
       }
     }
   }
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
 #pragma unroll
   for (int b = 0; b < B; ++b) ss[b] = 0.0f;
 
-  for (int c0 = 0; c0 < p.G; c0 += p.ch) {
+  auto chunk = [&](const int c0) {
     const int c1 = min(p.G, c0 + p.ch);
     const int n_c = (c1 - c0 - ksi + p.ks - 1) / p.ks;  // this wave's groups in the chunk (may be <= 0)
     const int n8 = (c1 - c0) * 16;                      // 16-byte items per staged row
@@ -346,6 +346,11 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
       }
       scale_acc(acc, dprev, sprev);
     }
+  };
+  if (p.ch >= p.G) {
+    chunk(0);  // the whole K in one chunk: straight-line code, no loop-carried waits
+  } else {
+    for (int c0 = 0; c0 < p.G; c0 += p.ch) chunk(c0);
   }
 
   // per-wave partial sums of x^2, and the tile rows of this wave
@@ -390,7 +395,7 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
     } else if constexpr (EPI == NQ_EPI_RESIDUAL_F16) {
       if (n < N) {
         half_t* yo = static_cast<half_t*>(p.y) + b * N + n;
-        const float r = i == tid ? e_res : static_cast<float>(*yo);  // prefetched for item tid
+        const float r = static_cast<float>(i == tid ? e_res : *yo);  // prefetched for item tid
         const half_t v = static_cast<half_t>(r + yv);
         *yo = v;
         if (p.y2) p.y2[b * N + n] = v;
@@ -559,12 +564,12 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvPara
   const uint32_t magic = opaque(0x64006400u);
 
   // the residual the epilogue adds to: one prefetched item per thread
-  float e_res = 0.0f;
+  half_t e_res = static_cast<half_t>(0.0f);  // kept as loaded: converting it here would wait for it
   if constexpr (EPI == NQ_EPI_RESIDUAL_F16) {
     if (tid < ntl * B * 16) {
       const int j = tid / (B * 16), b = (tid / 16) % B, rr = tid & 15;
       const int64_t n = tile_row_logical(p.kind, p.N, p.head_dim, t0 + j, rr);
-      if (n < p.N) e_res = static_cast<float>(static_cast<const half_t*>(p.y)[b * static_cast<int64_t>(p.N) + n]);
+      if (n < p.N) e_res = static_cast<const half_t*>(p.y)[b * static_cast<int64_t>(p.N) + n];
     }
   }
 
@@ -724,7 +729,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvPara
     } else if constexpr (EPI == NQ_EPI_RESIDUAL_F16) {
       if (n < N) {
         half_t* yo = static_cast<half_t*>(p.y) + b * N + n;
-        const float r = i == tid ? e_res : static_cast<float>(*yo);
+        const float r = static_cast<float>(i == tid ? e_res : *yo);
         const half_t v = static_cast<half_t>(r + yv);
         *yo = v;
         if (p.y2) p.y2[b * N + n] = v;

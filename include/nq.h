@@ -164,6 +164,25 @@ nq_status nq_gemv_w4a16(const void* packed, int32_t N, int32_t K, nq_mat_kind ki
                         const void* norm_gain, float eps, const void* bias, void* y,
                         nq_epilogue epi, void* stream);
 
+/*
+ * W4A16 GEMM for a chunk of M activation rows: y_m = W x_m for m < M, the same
+ * packed weights, arithmetic and epilogues as nq_gemv_w4a16 (fp32
+ * accumulation of exact INT4 codes times fp16 activations, the fp16 group
+ * scale applied to each group's fp32 partial sum) on the matrix cores with
+ * the rows as the MFMA columns. It is the projection step of the chunked
+ * prefill (nq_prefill): the prompt's tokens go through the fused Q/K/V/O and
+ * gate/up/down projections of "What it actually builds" a chunk at a time.
+ *
+ * M        : 1 .. 4096 rows.
+ * x        : device fp16 [M][K] (no RMSNorm prologue: normalise beforehand).
+ * bias, y, epi: as nq_gemv_w4a16 with batch = M.
+ * Errors: NQ_ERR_INVALID_ARG for null/misaligned pointers, K % 128, M out of
+ * 1..4096, or an epilogue that does not fit the kind; NQ_ERR_HIP on launch.
+ */
+nq_status nq_gemm_w4a16(const void* packed, int32_t N, int32_t K, nq_mat_kind kind,
+                        int32_t head_dim, int32_t M, const void* x, const void* bias,
+                        void* y, nq_epilogue epi, void* stream);
+
 /* ------------------------------------------------------------ model config */
 
 typedef struct nq_config {
@@ -248,6 +267,24 @@ nq_status nq_attn_decode(const nq_kv* kv, int32_t layer, int32_t batch, const vo
                          void* out, void* workspace, size_t ws_bytes, int32_t* err_flag,
                          void* stream);
 
+/*
+ * Causal paged attention of n_q consecutive queries of one sequence (the
+ * attention step of the chunked prefill): query row i sits at position
+ * start_pos + i and, for query head h with kv = h / (n_heads / n_kv_heads),
+ *   out[i][h] = sum_{t <= start_pos + i} softmax_t(q[i][h] . k_t / sqrt(d)) v_t
+ * (scaled dot-product attention with the causal mask, "Build Crude
+ * Implementations for Learning", section "nanoGPT level"). K and V of every
+ * position up to start_pos + n_q - 1 must already be in the pool; slots after
+ * that in the last page are never used, whatever they hold.
+ * q, out: device fp16 [n_q][n_heads][head_dim]; page_table: device int32
+ * [max_pages], this sequence's row. n_q: 1 .. 4096; start_pos >= 0 and
+ * start_pos + n_q <= max_pages * 16 (else NQ_ERR_OUT_OF_RANGE).
+ * err_flag: optional device int32 (a page id outside the pool ORs 2).
+ */
+nq_status nq_attn_prefill(const nq_kv* kv, int32_t layer, int32_t n_q, int32_t start_pos,
+                          const void* q, const int32_t* page_table, int32_t max_pages,
+                          void* out, int32_t* err_flag, void* stream);
+
 /* -------------------------------------------------------------- the model */
 
 typedef struct nq_model nq_model;
@@ -317,6 +354,51 @@ typedef struct nq_step_io {
  * bad io; NQ_ERR_HIP on launch failure.
  */
 nq_status nq_decode_step(nq_model* m, nq_kv* kv, const nq_step_io* io, void* stream);
+
+/* ---------------------------------------------------------- chunked prefill */
+
+/*
+ * Chunked prefill of one sequence's prompt (everything on the device): the
+ * tokens go through the model a chunk at a time instead of one decode step
+ * per token, which is what the time to first token depends on ("How To Build
+ * Your Own LLM Runtime From Scratch" (daily.dev), Summary; the runtime the
+ * pages describe is decode-only and its prefill is not described). For each
+ * chunk of up to `chunk` tokens, per layer: RMSNorm of the chunk's rows ->
+ * fused QKV GEMM + bias -> RoPE -> K/V page writes at their positions ->
+ * causal paged attention over positions [0, own position] -> O GEMM +
+ * residual -> RMSNorm -> gate/up GEMM + SwiGLU -> down GEMM + residual
+ * (7 kernels per layer). After the last chunk: final RMSNorm -> LM head of the
+ * last token -> greedy argmax (lowest index on ties), 2 kernels. The result
+ * equals feeding the tokens one by one through nq_decode_step up to rounding
+ * order, and the KV pages it writes are what decode steps then read.
+ */
+typedef struct nq_prefill_io {
+  int32_t n_tokens;          /* prompt tokens of this call, >= 1                                */
+  int32_t start_pos;         /* position of the first of them (K/V of earlier positions must
+                                already be in the pool), >= 0                                  */
+  const int32_t* tokens;     /* device int32 [n_tokens]                                        */
+  const int32_t* page_table; /* device int32 [max_pages]: this sequence's row                  */
+  int32_t max_pages;         /* start_pos + n_tokens <= max_pages * 16                         */
+  int32_t chunk;             /* tokens per chunk, 1 .. 4096                                    */
+  int32_t* next_token;       /* optional device int32: greedy token after the last prompt token */
+  int32_t* pos_out;          /* optional device int32: set to start_pos + n_tokens (the position
+                                of next_token in a following decode step)                     */
+  float* logits;             /* optional device float32 [vocab] at the last prompt token       */
+  void* layer_out;           /* optional device fp16 [layers][n_tokens][H]: hidden state after
+                                each layer (debug)                                             */
+  int32_t* err_flag;         /* optional device int32 (bits as nq_step_io); NULL uses a flag in
+                                the workspace                                                   */
+  void* workspace;           /* device, nq_prefill_workspace_bytes(cfg, chunk) bytes            */
+  size_t ws_bytes;
+} nq_prefill_io;
+
+/* Scratch bytes nq_prefill needs at a chunk size (0 for invalid arguments). */
+size_t nq_prefill_workspace_bytes(const nq_config* cfg, int32_t chunk);
+
+/* Errors: NQ_ERR_STATE if the model is not fully bound (its decode workspace
+ * is not needed); NQ_ERR_INVALID_ARG / NQ_ERR_OUT_OF_RANGE for bad io
+ * (positions past max_pages * 16 or cfg.max_pos); NQ_ERR_HIP on launch. */
+nq_status nq_prefill(nq_model* m, nq_kv* kv, const nq_prefill_io* io, void* stream);
 
 /* ---------------------------------------------------------- graph capture */
 

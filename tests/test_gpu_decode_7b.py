@@ -5,7 +5,9 @@ The full oracle run of a 7B-shaped model is too slow for a test, so the run is
 short (24 prompt tokens + 8 generated) and checked on samples the oracle can
 afford: three layers recomputed teacher-forced from the GPU's own layer inputs
 (first, middle, last), and the LM head + greedy choice recomputed from the
-GPU's final hidden state at every generated step over the full vocabulary."""
+GPU's final hidden state at every generated step over the full vocabulary.
+The chunked prefill is checked the same way on the 512-token prompt that the
+benchmark's time to first token uses (one chunk of 512 rows)."""
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -15,7 +17,7 @@ import torch
 import oracle
 import synth
 from oracle.model import OracleLayer, Dims, layer_causal
-from w4a16_gemv_paged_amd.engine import DeviceModel, KVCache, Stepper, run_greedy
+from w4a16_gemv_paged_amd.engine import DeviceModel, KVCache, Stepper, Prefill, run_greedy
 from gpu_util import quantize_rows, rel_inf, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
@@ -27,10 +29,19 @@ TOL_LAYER, TOL_LOGITS, MARGIN = 2e-3, 5e-3, 1e-2
 
 
 @pytest.fixture(scope="module")
-def run7b():
+def model7b():
     say("build 7B device model")
     head = synth.head_params(SHAPE, seed=0)
     dm = DeviceModel(SHAPE, lambda l: synth.layer_params(SHAPE, l, seed=0), head, max_batch=8, max_pos=4096)
+    yield dm, head
+    dm.close()
+    del dm
+    torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def run7b(model7b):
+    dm, head = model7b
     prompt = synth.prompt_ids(PROMPT, SHAPE.vocab, seed=2)
     # 52-page tables as in the timed run: attention splits the pages over 7
     # workgroups (all but the first empty at this length) and merges them
@@ -47,9 +58,6 @@ def run7b():
         torch.cuda.synchronize()
         st.close()
         kv.close()
-    dm.close()
-    del dm
-    torch.cuda.empty_cache()
     return prompt, head, out[False], out[True]
 
 
@@ -92,3 +100,51 @@ def test_7b_head_logits_and_tokens(run7b):
             clear += 1
             assert gpu["tokens"][0][i] == oracle.argmax_lowest(z), (i, t)
     assert clear >= GEN // 2
+
+
+PF_PROMPT = 512
+
+
+@pytest.fixture(scope="module")
+def prefill7b(model7b):
+    dm, head = model7b
+    prompt = synth.prompt_ids(PF_PROMPT, SHAPE.vocab, seed=4)
+    pt, total = synth.decode_page_tables(1, PF_PROMPT // 16 + 2, seed=3, spare_pages=2)
+    kv = KVCache(dm, total, poison=True)
+    pf = Prefill(dm, kv, PF_PROMPT)
+    cfg = dm.cfg
+    lo = torch.empty(cfg.layers, PF_PROMPT, cfg.hidden, dtype=torch.float16, device="cuda")
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    nt = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    say("7B prefill", PF_PROMPT)
+    pf.run(prompt, torch.from_numpy(pt[0]).cuda(), 0, nt, None, logits, lo)
+    pf.check()
+    torch.cuda.synchronize()
+    out = dict(layer_out=lo.cpu().numpy(), logits=logits.cpu().numpy(), next=int(nt.cpu()[0]))
+    kv.close()
+    return prompt, head, out
+
+
+def test_7b_prefill_layers_teacher_forced(prefill7b):
+    prompt, head, gpu = prefill7b
+    lo = gpu["layer_out"]                                            # [L, T, H]
+    dims = Dims(SHAPE.hidden, SHAPE.intermediate, SHAPE.n_heads, SHAPE.n_kv_heads, SHAPE.head_dim, SHAPE.vocab)
+    for li in LAYERS:
+        say("oracle prefill layer", li)
+        L = OracleLayer(synth.layer_params(SHAPE, li, seed=0), quant=quantize_rows)
+        x = head["embed"][np.array(prompt)] if li == 0 else lo[li - 1]
+        ref = layer_causal(L, dims, x)
+        errs = [rel_inf(lo[li, t], ref[t]) for t in range(PF_PROMPT)]
+        assert max(errs) < TOL_LAYER, (li, int(np.argmax(errs)), max(errs))
+        L.drop_cache()
+
+
+def test_7b_prefill_head(prefill7b):
+    prompt, head, gpu = prefill7b
+    q, s = quantize_rows(head["lm_head"])
+    x = oracle.rmsnorm(gpu["layer_out"][-1, -1], head["g_final"], 1e-6).astype(np.float64)
+    z = oracle.dequantize_w4(q, s) @ x
+    assert rel_inf(gpu["logits"], z) < TOL_LOGITS
+    top2 = np.sort(z)[-2:]
+    if top2[1] - top2[0] > MARGIN:
+        assert gpu["next"] == oracle.argmax_lowest(z)

@@ -26,6 +26,7 @@ __all__ = [
     "nq_rope_table_bytes", "nq_rope_table_fill", "nq_model_bind_rope", "nq_workspace_bytes",
     "nq_model_bind_workspace", "nq_model_destroy", "nq_decode_step", "nq_graph_capture",
     "nq_graph_launch", "nq_graph_kernel_count", "nq_graph_destroy", "nq_check_device_error",
+    "nq_gemm_w4a16", "nq_attn_prefill", "NQPrefillIO", "nq_prefill_workspace_bytes", "nq_prefill",
     "header_symbols",
 ]
 
@@ -72,6 +73,14 @@ class NQStepIO(ctypes.Structure):
                 ("err_flag", ctypes.c_void_p)]
 
 
+class NQPrefillIO(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int32), ("start_pos", ctypes.c_int32), ("tokens", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("next_token", ctypes.c_void_p), ("pos_out", ctypes.c_void_p), ("logits", ctypes.c_void_p),
+                ("layer_out", ctypes.c_void_p), ("err_flag", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("ws_bytes", ctypes.c_size_t)]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _S = ctypes.c_size_t
@@ -109,6 +118,10 @@ _SIGS = {
     "nq_graph_kernel_count": (_I, [_P]),
     "nq_graph_destroy": (None, [_P]),
     "nq_check_device_error": (_I, [_P, _P]),
+    "nq_gemm_w4a16": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P]),
+    "nq_attn_prefill": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P, _P]),
+    "nq_prefill_workspace_bytes": (_S, [_CFG, _I]),
+    "nq_prefill": (_I, [_P, _P, ctypes.POINTER(NQPrefillIO), _P]),
 }
 
 _lib = None
@@ -215,6 +228,11 @@ def nq_gemv_w4a16(packed, N, K, kind, head_dim, batch, x, norm_gain, eps, bias, 
                                _ptr(bias), _ptr(y), epi, _stream(stream)), "nq_gemv_w4a16")
 
 
+def nq_gemm_w4a16(packed, N, K, kind, head_dim, M, x, bias, y, epi, stream=None):
+    _check(lib().nq_gemm_w4a16(_ptr(packed), N, K, kind, head_dim, M, _ptr(x), _ptr(bias), _ptr(y), epi,
+                               _stream(stream)), "nq_gemm_w4a16")
+
+
 def nq_config_check(cfg: NQConfig) -> None:
     _check(lib().nq_config_check(ctypes.byref(cfg)), "nq_config_check")
 
@@ -248,6 +266,11 @@ def nq_attn_decode(kv, layer, batch, q, page_table, max_pages, lens, out, worksp
                    stream=None):
     _check(lib().nq_attn_decode(kv, layer, batch, _ptr(q), _ptr(page_table), max_pages, _ptr(lens), _ptr(out),
                                 _ptr(workspace), ws_bytes, _ptr(err_flag), _stream(stream)), "nq_attn_decode")
+
+
+def nq_attn_prefill(kv, layer, n_q, start_pos, q, page_table, max_pages, out, err_flag=None, stream=None):
+    _check(lib().nq_attn_prefill(kv, layer, n_q, start_pos, _ptr(q), _ptr(page_table), max_pages, _ptr(out),
+                                 _ptr(err_flag), _stream(stream)), "nq_attn_prefill")
 
 
 # ------------------------------------------------------------------ model, step, graph
@@ -316,3 +339,13 @@ def nq_graph_destroy(g) -> None:
 
 def nq_check_device_error(err_flag, stream=None) -> None:
     _check(lib().nq_check_device_error(_ptr(err_flag), _stream(stream)), "nq_check_device_error")
+
+
+# ------------------------------------------------------------------ chunked prefill
+
+def nq_prefill_workspace_bytes(cfg: NQConfig, chunk: int) -> int:
+    return lib().nq_prefill_workspace_bytes(ctypes.byref(cfg), chunk)
+
+
+def nq_prefill(m, kv, io: NQPrefillIO, stream=None) -> None:
+    _check(lib().nq_prefill(m, kv, ctypes.byref(io), _stream(stream)), "nq_prefill")

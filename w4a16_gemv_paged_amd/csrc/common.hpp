@@ -53,6 +53,7 @@ inline size_t codes_bytes(int32_t N, int32_t K) {
 // Internal epilogues beyond the public nq_epilogue values.
 enum InternalEpi : int {
   EPI_QKV_ROPE_KV = 16,  // bias, RoPE on q/k, q -> qbuf, k/v -> KV pool (decode step)
+  EPI_PREFILL_QKV = 17,  // the same for the rows of a prefill chunk, positions pos0 + row, one sequence
 };
 
 struct GemvArgs {
@@ -117,8 +118,52 @@ hipError_t launch_kv_append(void* k_pool, void* v_pool, int32_t batch, int32_t n
                             int32_t num_pages, const int32_t* pos, const void* k, const void* v,
                             int32_t* err, hipStream_t s);
 
+// tokens[b] = greedy token; then pos[b] += 1 (and hist[b][pos+1] = token), or
+// pos[b] = pos_set when pos_set >= 0 (pos may be null then).
 hipError_t launch_argmax_finalize(const float* vals, const int32_t* idx, int32_t partials, int32_t batch,
-                                  int32_t* tokens, int32_t* pos, int32_t* hist, int32_t hist_len, hipStream_t s);
+                                  int32_t* tokens, int32_t* pos, int32_t* hist, int32_t hist_len, int32_t pos_set,
+                                  hipStream_t s);
+
+// ------------------------------------------------------------ chunked prefill
+
+constexpr int32_t kPrefillMaxChunk = 4096;  // rows of one prefill GEMM / attention call
+
+struct GemmArgs {
+  const void* packed = nullptr;
+  int32_t N = 0, K = 0, kind = 0, head_dim = 0, M = 0;
+  const void* x = nullptr;          // fp16 [M][K]
+  const void* bias = nullptr;       // fp16 [N]
+  void* y = nullptr;
+  void* y2 = nullptr;               // RESIDUAL: optional copy of the result [M][N]
+  int epi = 0;
+  int32_t pos0 = 0;                 // EPI_PREFILL_QKV
+  const int32_t* page_table = nullptr;
+  int32_t max_pages = 0, num_pages = 0, n_heads = 0, n_kv = 0;
+  void* kv_k = nullptr;
+  void* kv_v = nullptr;
+  const float* rope = nullptr;
+  int32_t max_pos = 0;
+  int32_t* err = nullptr;
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+// xn[m] = fp16(x / sqrt(mean(x^2) + eps) * gain) for m < M, with x = h[m], or
+// x = embed[tokens[m]] when embed is given (then h[m] = x is stored too).
+hipError_t launch_rmsnorm_rows(const void* h_in, const void* embed, const int32_t* tokens, int32_t vocab,
+                               void* h_out, const void* gain, float eps, void* xn, int32_t M, int32_t H,
+                               int32_t* err, hipStream_t s);
+
+struct PrefillAttnArgs {
+  const void* q = nullptr;          // fp16 [M][nh][d]
+  const void* k_pool = nullptr;
+  const void* v_pool = nullptr;
+  const int32_t* page_table = nullptr;  // one sequence: [max_pages]
+  int32_t max_pages = 0, num_pages = 0;
+  int32_t M = 0, pos0 = 0, n_heads = 0, n_kv = 0, head_dim = 0;
+  void* out = nullptr;              // fp16 [M][nh][d]
+  int32_t* err = nullptr;
+};
+hipError_t launch_attn_prefill(const PrefillAttnArgs& a, hipStream_t s);
 
 hipError_t launch_unpack_dev(const void* packed, int32_t N, int32_t K, int32_t kind,
                              int32_t head_dim, int8_t* q_out, uint16_t* s_out, hipStream_t s);

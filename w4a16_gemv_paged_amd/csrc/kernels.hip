@@ -18,56 +18,9 @@
 // * Small kernels: embedding gather, KV append, argmax finalize, device unpack.
 #include <algorithm>
 
-#include "common.hpp"
+#include "device.hpp"
 
 namespace nq {
-
-typedef _Float16 half_t;
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
-
-// ORs error bits into the optional device flag.
-__device__ __forceinline__ void raise_flag(int32_t* err, int bits) {
-  if (err) atomicOr(err, bits);
-}
-
-// Orders this lane's LDS accesses against the other lanes of its own wave
-// (wave-local sync; never a block barrier).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// One 32-bit word of eight offset-binary nibbles -> four pairs of exact fp16
-// codes: (q[k], q[k+1]), (q[k+2], q[k+3]), (q[k+4], q[k+5]), (q[k+6], q[k+7]).
-// A nibble n in bits 0-3 of a 16-bit half, OR'ed with 0x6400, is the half
-// 1024 + n; subtracting 1032 leaves q = n - 8 exactly. A nibble in bits 4-7
-// gives 1024 + 16n; (1024 + 16n) / 16 - 72 = n - 8, also exact. ``magic``
-// (0x64006400) is passed in a register so that each mask-and-insert is a
-// single v_and_or_b32 (gfx9 VOP3 cannot take two literal constants).
-__device__ __forceinline__ void unpack8(uint32_t w, uint32_t magic, h2 (&o)[4]) {
-  const h2 off_lo = {static_cast<half_t>(-1032.0f), static_cast<half_t>(-1032.0f)};
-  const h2 sixteenth = {static_cast<half_t>(0.0625f), static_cast<half_t>(0.0625f)};
-  const h2 off_hi = {static_cast<half_t>(-72.0f), static_cast<half_t>(-72.0f)};
-  const uint32_t w8 = w >> 8;
-  o[0] = as_h2((w & 0x000F000Fu) | magic) + off_lo;
-  o[1] = __builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | magic), sixteenth, off_hi);
-  o[2] = as_h2((w8 & 0x000F000Fu) | magic) + off_lo;
-  o[3] = __builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | magic), sixteenth, off_hi);
-}
-
-__device__ __forceinline__ void unpack8(uint32_t w, h2 (&o)[4]) { unpack8(w, 0x64006400u, o); }
-
-__device__ __forceinline__ float dot2(h2 a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(a, as_h2(b), c, false);
-}
-
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
 
 // ============================================================== GEMV
 //
@@ -82,14 +35,8 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
 // row are scaled by that row's fp16 group scale in fp32. Slices of a tile are
 // summed through LDS, then the fused epilogue runs on (tile, batch, row) items.
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kDepth = 8;                   // 1 KiB weight loads in flight per wave
 constexpr int kDmaBatch = 8;                // activation copies issued back to back per wave
-constexpr int kBufferFlags = 0x00020000;    // gfx9 raw buffer descriptor word 3
 constexpr size_t kLdsX = 56 * 1024;         // LDS budget for staged activations and gain
 
 struct GemvParams {
@@ -137,24 +84,6 @@ __device__ __forceinline__ f4 gemv_block_mfma(const u32x4& w, const half_t* xg, 
   }
   return d;
 }
-
-// acc[i] += d[i] * scale of row 4*(l/16)+i (fp16 scales of four rows in sc)
-__device__ __forceinline__ void scale_acc(f4& acc, const f4& d, const u32x2& sc) {
-  const h2 s01 = as_h2(sc.x), s23 = as_h2(sc.y);
-  acc[0] = fmaf(d[0], static_cast<float>(s01[0]), acc[0]);
-  acc[1] = fmaf(d[1], static_cast<float>(s01[1]), acc[1]);
-  acc[2] = fmaf(d[2], static_cast<float>(s23[0]), acc[2]);
-  acc[3] = fmaf(d[3], static_cast<float>(s23[1]), acc[3]);
-}
-
-// Greedy tie rule: larger value wins, equal values go to the lower index.
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
-
-// s_waitcnt immediates (gfx9 encoding): wait for LDS/scalar memory only, or
-// for LDS/scalar memory and until at most n vector-memory operations are
-// outstanding.
-constexpr int kWaitLgkm0 = 0xC07F;
-constexpr int wait_vm_lgkm0(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
 
 template <int B, int EPI, bool GAIN>
 __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
@@ -987,8 +916,6 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
 // (max, sum, output) partials and the combine kernel merges them with the
 // log-sum-exp rule.
 
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-
 constexpr int kAttnWaves = 8;
 constexpr int kMaxSplits = 64;
 constexpr int kMaxPagesPerWave = 64;  // page ids held one per lane
@@ -1313,10 +1240,10 @@ hipError_t launch_kv_append(void* k_pool, void* v_pool, int32_t batch, int32_t n
 
 // grid (B), 1024 threads: reduce the LM head's per-workgroup (max, index)
 // partials of one batch row, write the greedy token, its history entry, and
-// advance the position.
+// advance the position (or set it to pos_set >= 0; pos may be null then).
 __global__ __launch_bounds__(1024) void argmax_finalize_kernel(const float* vals, const int32_t* idx, int P,
                                                                int32_t* tokens, int32_t* pos, int32_t* hist,
-                                                               int hist_len) {
+                                                               int hist_len, int pos_set) {
   __shared__ float sv[16];
   __shared__ int si[16];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1350,16 +1277,22 @@ __global__ __launch_bounds__(1024) void argmax_finalize_kernel(const float* vals
         bi = si[k];
       }
     const int tok = bi == 0x7fffffff ? 0 : bi;
-    const int ps = pos[b];
     tokens[b] = tok;
-    if (hist && ps + 1 >= 0 && ps + 1 < hist_len) hist[static_cast<int64_t>(b) * hist_len + ps + 1] = tok;
-    pos[b] = ps + 1;
+    if (pos_set >= 0) {
+      if (pos) pos[b] = pos_set;
+    } else {
+      const int ps = pos[b];
+      if (hist && ps + 1 >= 0 && ps + 1 < hist_len) hist[static_cast<int64_t>(b) * hist_len + ps + 1] = tok;
+      pos[b] = ps + 1;
+    }
   }
 }
 
 hipError_t launch_argmax_finalize(const float* vals, const int32_t* idx, int32_t partials, int32_t batch,
-                                  int32_t* tokens, int32_t* pos, int32_t* hist, int32_t hist_len, hipStream_t s) {
-  argmax_finalize_kernel<<<dim3(batch), dim3(1024), 0, s>>>(vals, idx, partials, tokens, pos, hist, hist_len);
+                                  int32_t* tokens, int32_t* pos, int32_t* hist, int32_t hist_len, int32_t pos_set,
+                                  hipStream_t s) {
+  argmax_finalize_kernel<<<dim3(batch), dim3(1024), 0, s>>>(vals, idx, partials, tokens, pos, hist, hist_len,
+                                                            pos_set);
   return hipGetLastError();
 }
 

@@ -241,8 +241,176 @@ int enqueue_step(nq_model* m, nq_kv* kv, const nq_step_io* io, hipStream_t s) {
   lm.err = err;
   if ((e = launch_gemv(lm, s)) != hipSuccess) return hip_fail(e, "lm head launch"), -1;
   e = launch_argmax_finalize(w.amax_val, w.amax_idx, gemv_grid_size(c.vocab, c.hidden, B), B, io->tokens, io->pos,
-                             io->token_hist, io->hist_len, s);
+                             io->token_hist, io->hist_len, -1, s);
   if (e != hipSuccess) return hip_fail(e, "argmax launch"), -1;
+  return launches + 2;
+}
+
+struct PrefillWs {
+  int32_t* err;
+  int32_t* tok;  // next token when the caller passes none
+  void* h;
+  void* xn;
+  void* qbuf;
+  void* attn_o;
+  void* act;
+  float* amax_val;
+  int32_t* amax_idx;
+  size_t total;
+};
+
+PrefillWs carve_prefill(const nq_config& c, int32_t chunk, uint8_t* base) {
+  PrefillWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    uint8_t* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  const size_t qd = static_cast<size_t>(c.n_heads) * c.head_dim;
+  uint8_t* flags = take(256);
+  w.err = reinterpret_cast<int32_t*>(flags);
+  w.tok = reinterpret_cast<int32_t*>(flags ? flags + 64 : nullptr);
+  w.h = take(static_cast<size_t>(chunk) * c.hidden * 2);
+  w.xn = take(static_cast<size_t>(chunk) * c.hidden * 2);
+  w.qbuf = take(static_cast<size_t>(chunk) * qd * 2);
+  w.attn_o = take(static_cast<size_t>(chunk) * qd * 2);
+  w.act = take(static_cast<size_t>(chunk) * c.intermediate * 2);
+  const int64_t P = gemv_grid_size(c.vocab, c.hidden, 1);
+  w.amax_val = reinterpret_cast<float*>(take(static_cast<size_t>(P) * 4));
+  w.amax_idx = reinterpret_cast<int32_t*>(take(static_cast<size_t>(P) * 4));
+  w.total = off;
+  return w;
+}
+
+// Enqueue a chunked prefill. Returns the number of kernels launched or -1.
+int enqueue_prefill(nq_model* m, nq_kv* kv, const nq_prefill_io* io, hipStream_t s) {
+  const nq_config& c = m->cfg;
+  PrefillWs w = carve_prefill(c, io->chunk, static_cast<uint8_t*>(io->workspace));
+  int32_t* err = io->err_flag ? io->err_flag : w.err;
+  const int qkv_n = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const size_t lp = layer_pool_elems(c, kv->num_pages);
+  uint16_t* pool = static_cast<uint16_t*>(kv->pool);
+  const int n = io->n_tokens;
+  int launches = 0, mc = 0;
+  hipError_t e = hipSuccess;
+  for (int c0 = 0; c0 < n; c0 += io->chunk) {
+    mc = std::min(io->chunk, n - c0);
+    const int pos0 = io->start_pos + c0;
+    for (int l = 0; l < c.layers; ++l) {
+      const nq_layer_ptrs& L = m->layers[l];
+      uint16_t* kbase = pool + static_cast<size_t>(l) * 2 * lp;
+      uint16_t* vbase = kbase + lp;
+      // layer 0 gathers the chunk's embedding rows into the residual stream
+      if ((e = launch_rmsnorm_rows(w.h, l == 0 ? m->embed : nullptr, io->tokens + c0, c.vocab, w.h, L.attn_norm,
+                                   c.rms_eps, w.xn, mc, c.hidden, err, s)) != hipSuccess)
+        return hip_fail(e, "prefill norm launch"), -1;
+
+      GemmArgs q{};
+      q.packed = L.qkv_packed;
+      q.N = qkv_n;
+      q.K = c.hidden;
+      q.kind = NQ_MAT_QKV;
+      q.head_dim = c.head_dim;
+      q.M = mc;
+      q.x = w.xn;
+      q.bias = L.qkv_bias;
+      q.y = w.qbuf;
+      q.epi = EPI_PREFILL_QKV;
+      q.pos0 = pos0;
+      q.page_table = io->page_table;
+      q.max_pages = io->max_pages;
+      q.num_pages = kv->num_pages;
+      q.n_heads = c.n_heads;
+      q.n_kv = c.n_kv_heads;
+      q.kv_k = kbase;
+      q.kv_v = vbase;
+      q.rope = m->rope;
+      q.max_pos = c.max_pos;
+      q.err = err;
+      if ((e = launch_gemm(q, s)) != hipSuccess) return hip_fail(e, "prefill qkv launch"), -1;
+
+      PrefillAttnArgs at{};
+      at.q = w.qbuf;
+      at.k_pool = kbase;
+      at.v_pool = vbase;
+      at.page_table = io->page_table;
+      at.max_pages = io->max_pages;
+      at.num_pages = kv->num_pages;
+      at.M = mc;
+      at.pos0 = pos0;
+      at.n_heads = c.n_heads;
+      at.n_kv = c.n_kv_heads;
+      at.head_dim = c.head_dim;
+      at.out = w.attn_o;
+      at.err = err;
+      if ((e = launch_attn_prefill(at, s)) != hipSuccess) return hip_fail(e, "prefill attention launch"), -1;
+
+      GemmArgs o{};
+      o.packed = L.o_packed;
+      o.N = c.hidden;
+      o.K = c.n_heads * c.head_dim;
+      o.kind = NQ_MAT_PLAIN;
+      o.M = mc;
+      o.x = w.attn_o;
+      o.y = w.h;
+      o.epi = NQ_EPI_RESIDUAL_F16;
+      o.err = err;
+      if ((e = launch_gemm(o, s)) != hipSuccess) return hip_fail(e, "prefill o launch"), -1;
+
+      if ((e = launch_rmsnorm_rows(w.h, nullptr, nullptr, c.vocab, nullptr, L.mlp_norm, c.rms_eps, w.xn, mc,
+                                   c.hidden, err, s)) != hipSuccess)
+        return hip_fail(e, "prefill norm launch"), -1;
+
+      GemmArgs gu{};
+      gu.packed = L.gate_up_packed;
+      gu.N = 2 * c.intermediate;
+      gu.K = c.hidden;
+      gu.kind = NQ_MAT_GATE_UP;
+      gu.M = mc;
+      gu.x = w.xn;
+      gu.y = w.act;
+      gu.epi = NQ_EPI_SWIGLU_F16;
+      gu.err = err;
+      if ((e = launch_gemm(gu, s)) != hipSuccess) return hip_fail(e, "prefill gate/up launch"), -1;
+
+      GemmArgs dn{};
+      dn.packed = L.down_packed;
+      dn.N = c.hidden;
+      dn.K = c.intermediate;
+      dn.kind = NQ_MAT_PLAIN;
+      dn.M = mc;
+      dn.x = w.act;
+      dn.y = w.h;
+      dn.y2 = io->layer_out
+                  ? static_cast<uint16_t*>(io->layer_out) + (static_cast<size_t>(l) * n + c0) * c.hidden
+                  : nullptr;
+      dn.epi = NQ_EPI_RESIDUAL_F16;
+      dn.err = err;
+      if ((e = launch_gemm(dn, s)) != hipSuccess) return hip_fail(e, "prefill down launch"), -1;
+      launches += 7;
+    }
+  }
+  // the first generated token: LM head of the prompt's last row
+  GemvArgs lm{};
+  lm.packed = m->lm;
+  lm.N = c.vocab;
+  lm.K = c.hidden;
+  lm.kind = NQ_MAT_LM_HEAD;
+  lm.batch = 1;
+  lm.x = static_cast<const uint16_t*>(w.h) + static_cast<size_t>(mc - 1) * c.hidden;
+  lm.norm_gain = m->final_norm;
+  lm.eps = c.rms_eps;
+  lm.y = io->logits;
+  lm.epi = NQ_EPI_STORE_F32;
+  lm.amax_val = w.amax_val;
+  lm.amax_idx = w.amax_idx;
+  lm.err = err;
+  if ((e = launch_gemv(lm, s)) != hipSuccess) return hip_fail(e, "prefill lm head launch"), -1;
+  e = launch_argmax_finalize(w.amax_val, w.amax_idx, gemv_grid_size(c.vocab, c.hidden, 1), 1,
+                             io->next_token ? io->next_token : w.tok, io->pos_out, nullptr, 0,
+                             io->start_pos + n, s);
+  if (e != hipSuccess) return hip_fail(e, "prefill argmax launch"), -1;
   return launches + 2;
 }
 
@@ -282,6 +450,37 @@ nq_status nq_gemv_w4a16(const void* packed, int32_t N, int32_t K, nq_mat_kind ki
   a.epi = epi;
   hipError_t e = launch_gemv(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "nq_gemv_w4a16 launch");
+  return NQ_OK;
+}
+
+nq_status nq_gemm_w4a16(const void* packed, int32_t N, int32_t K, nq_mat_kind kind, int32_t head_dim, int32_t M,
+                        const void* x, const void* bias, void* y, nq_epilogue epi, void* stream) {
+  nq_status st = check_pack_args(N, K, kGroup, kind, head_dim);
+  if (st != NQ_OK) return st;
+  if (!packed || !x || !y) return fail(NQ_ERR_INVALID_ARG, "nq_gemm_w4a16: null packed, x or y");
+  if (!aligned16(packed) || !aligned16(x))
+    return fail(NQ_ERR_INVALID_ARG, "nq_gemm_w4a16: packed and x must be 16-byte aligned");
+  if (M < 1 || M > kPrefillMaxChunk) return fail(NQ_ERR_INVALID_ARG, "M %d outside 1..%d", M, kPrefillMaxChunk);
+  if (epi < NQ_EPI_STORE_F16 || epi > NQ_EPI_STORE_F32)
+    return fail(NQ_ERR_INVALID_ARG, "unknown epilogue %d", static_cast<int>(epi));
+  if (epi == NQ_EPI_SWIGLU_F16 && kind != NQ_MAT_GATE_UP)
+    return fail(NQ_ERR_INVALID_ARG, "SwiGLU epilogue needs a GATE_UP matrix");
+  if (epi != NQ_EPI_SWIGLU_F16 && kind == NQ_MAT_GATE_UP)
+    return fail(NQ_ERR_INVALID_ARG, "a GATE_UP matrix needs the SwiGLU epilogue");
+  if (epi == NQ_EPI_BIAS_F16 && !bias) return fail(NQ_ERR_INVALID_ARG, "bias epilogue needs bias");
+  GemmArgs a{};
+  a.packed = packed;
+  a.N = N;
+  a.K = K;
+  a.kind = kind;
+  a.head_dim = head_dim;
+  a.M = M;
+  a.x = x;
+  a.bias = bias;
+  a.y = y;
+  a.epi = epi;
+  hipError_t e = launch_gemm(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "nq_gemm_w4a16 launch");
   return NQ_OK;
 }
 
@@ -386,6 +585,40 @@ nq_status nq_attn_decode(const nq_kv* kv, int32_t layer, int32_t batch, const vo
   return NQ_OK;
 }
 
+nq_status nq_attn_prefill(const nq_kv* kv, int32_t layer, int32_t n_q, int32_t start_pos, const void* q,
+                          const int32_t* page_table, int32_t max_pages, void* out, int32_t* err_flag,
+                          void* stream) {
+  if (!kv) return fail(NQ_ERR_INVALID_ARG, "null kv");
+  if (layer < 0 || layer >= kv->cfg.layers) return fail(NQ_ERR_OUT_OF_RANGE, "layer %d out of range", layer);
+  if (n_q < 1 || n_q > kPrefillMaxChunk) return fail(NQ_ERR_INVALID_ARG, "n_q %d outside 1..%d", n_q, kPrefillMaxChunk);
+  if (start_pos < 0) return fail(NQ_ERR_INVALID_ARG, "start_pos must be >= 0");
+  if (max_pages < 1) return fail(NQ_ERR_INVALID_ARG, "max_pages must be >= 1");
+  if (!q || !page_table || !out) return fail(NQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(q) || !aligned16(out)) return fail(NQ_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (static_cast<int64_t>(start_pos) + n_q > static_cast<int64_t>(max_pages) * kPageTokens)
+    return fail(NQ_ERR_OUT_OF_RANGE, "positions up to %lld exceed max_pages * 16",
+                static_cast<long long>(start_pos) + n_q - 1);
+  const size_t lp = layer_pool_elems(kv->cfg, kv->num_pages);
+  const uint16_t* kb = static_cast<const uint16_t*>(kv->pool) + static_cast<size_t>(layer) * 2 * lp;
+  PrefillAttnArgs a{};
+  a.q = q;
+  a.k_pool = kb;
+  a.v_pool = kb + lp;
+  a.page_table = page_table;
+  a.max_pages = max_pages;
+  a.num_pages = kv->num_pages;
+  a.M = n_q;
+  a.pos0 = start_pos;
+  a.n_heads = kv->cfg.n_heads;
+  a.n_kv = kv->cfg.n_kv_heads;
+  a.head_dim = kv->cfg.head_dim;
+  a.out = out;
+  a.err = err_flag;
+  hipError_t e = launch_attn_prefill(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  return NQ_OK;
+}
+
 nq_status nq_model_create(const nq_config* cfg, nq_model** out) {
   nq_status st = nq_config_check(cfg);
   if (st != NQ_OK) return st;
@@ -449,6 +682,41 @@ nq_status nq_decode_step(nq_model* m, nq_kv* kv, const nq_step_io* io, void* str
   nq_status st = check_model_ready(m, kv, io);
   if (st != NQ_OK) return st;
   if (enqueue_step(m, kv, io, static_cast<hipStream_t>(stream)) < 0) return NQ_ERR_HIP;
+  return NQ_OK;
+}
+
+size_t nq_prefill_workspace_bytes(const nq_config* cfg, int32_t chunk) {
+  if (nq_config_check(cfg) != NQ_OK || chunk < 1 || chunk > kPrefillMaxChunk) return 0;
+  return carve_prefill(*cfg, chunk, nullptr).total;
+}
+
+nq_status nq_prefill(nq_model* m, nq_kv* kv, const nq_prefill_io* io, void* stream) {
+  if (!m || !kv || !io) return fail(NQ_ERR_INVALID_ARG, "null model, kv or io");
+  for (int i = 0; i < m->cfg.layers; ++i)
+    if (!m->bound[i]) return fail(NQ_ERR_STATE, "layer %d not bound", i);
+  if (!m->embed || !m->final_norm || !m->lm) return fail(NQ_ERR_STATE, "head not bound");
+  if (!m->rope) return fail(NQ_ERR_STATE, "RoPE table not bound");
+  const nq_config& c = m->cfg;
+  if (c.layers != kv->cfg.layers || c.n_kv_heads != kv->cfg.n_kv_heads || c.head_dim != kv->cfg.head_dim)
+    return fail(NQ_ERR_INVALID_ARG, "KV cache config does not match the model");
+  if (io->n_tokens < 1) return fail(NQ_ERR_INVALID_ARG, "n_tokens must be >= 1");
+  if (io->start_pos < 0) return fail(NQ_ERR_INVALID_ARG, "start_pos must be >= 0");
+  if (io->chunk < 1 || io->chunk > kPrefillMaxChunk)
+    return fail(NQ_ERR_INVALID_ARG, "chunk %d outside 1..%d", io->chunk, kPrefillMaxChunk);
+  if (io->max_pages < 1) return fail(NQ_ERR_INVALID_ARG, "max_pages must be >= 1");
+  if (!io->tokens || !io->page_table || !io->workspace)
+    return fail(NQ_ERR_INVALID_ARG, "tokens, page_table and workspace are required");
+  if (!aligned16(io->workspace)) return fail(NQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (io->ws_bytes < carve_prefill(c, io->chunk, nullptr).total)
+    return fail(NQ_ERR_INVALID_ARG, "prefill workspace too small: %zu < %zu bytes", io->ws_bytes,
+                carve_prefill(c, io->chunk, nullptr).total);
+  const int64_t end = static_cast<int64_t>(io->start_pos) + io->n_tokens;
+  if (end > static_cast<int64_t>(io->max_pages) * kPageTokens)
+    return fail(NQ_ERR_OUT_OF_RANGE, "positions up to %lld exceed max_pages * 16", static_cast<long long>(end - 1));
+  if (end > c.max_pos)
+    return fail(NQ_ERR_OUT_OF_RANGE, "positions up to %lld exceed max_pos %d", static_cast<long long>(end - 1),
+                c.max_pos);
+  if (enqueue_prefill(m, kv, io, static_cast<hipStream_t>(stream)) < 0) return NQ_ERR_HIP;
   return NQ_OK;
 }
 

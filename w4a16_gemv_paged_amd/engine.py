@@ -17,7 +17,8 @@ from . import (NQConfig, NQLayerPtrs, NQStepIO, NQ_MAT_PLAIN, NQ_MAT_QKV, NQ_MAT
                nq_pack_weights, nq_model_create, nq_model_bind_layer, nq_model_bind_head, nq_model_bind_rope,
                nq_rope_table_fill, nq_workspace_bytes, nq_model_bind_workspace, nq_model_destroy,
                nq_kv_pool_bytes, nq_kv_alloc, nq_kv_free, nq_decode_step, nq_graph_capture, nq_graph_launch,
-               nq_graph_destroy, nq_graph_kernel_count, nq_check_device_error)
+               nq_graph_destroy, nq_graph_kernel_count, nq_check_device_error, NQPrefillIO,
+               nq_prefill_workspace_bytes, nq_prefill)
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -154,8 +155,33 @@ class Stepper:
             self.graph = None
 
 
+class Prefill:
+    """Workspace and buffers of the chunked prefill (``nq_prefill``) at one chunk size."""
+
+    def __init__(self, model: DeviceModel, kv: KVCache, chunk: int):
+        self.model, self.kv, self.chunk = model, kv, chunk
+        dev = model.device
+        self.ws_bytes = nq_prefill_workspace_bytes(model.cfg, chunk)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def run(self, tokens, page_row, start_pos: int = 0, next_token=None, pos_out=None, logits=None,
+            layer_out=None, stream=None):
+        """Prefills ``tokens`` (positions start_pos..) of the sequence whose page-table row is ``page_row``
+        (a device int32 tensor). Outputs go to the given device tensors (each optional)."""
+        toks = torch.as_tensor(np.asarray(tokens, np.int32)).to(self.model.device)
+        p = lambda t: t.data_ptr() if t is not None else None
+        io = NQPrefillIO(len(tokens), start_pos, p(toks), p(page_row), page_row.numel(), self.chunk, p(next_token),
+                         p(pos_out), p(logits), p(layer_out), p(self.err), p(self.ws), self.ws_bytes)
+        nq_prefill(self.model.handle, self.kv.handle, io, stream)
+        self._toks = toks  # alive until the stream has used it
+
+    def check(self, stream=None):
+        nq_check_device_error(self.err, stream)
+
+
 def run_greedy(st: Stepper, prompts, n_gen: int, use_graph: bool = False, stream=None,
-               record_logits: bool = False, record_layers: bool = False):
+               record_logits: bool = False, record_layers: bool = False, prefill_chunk: int | None = None):
     """Greedy decode of ``batch`` sequences in lockstep, one token per step.
 
     prompts: list of int sequences (ragged allowed). Sequence b goes through its
@@ -164,7 +190,14 @@ def run_greedy(st: Stepper, prompts, n_gen: int, use_graph: bool = False, stream
     is shorter start generating earlier and stop after n_gen tokens; they keep
     stepping (their extra tokens are ignored) until every sequence is done.
     Returns generated tokens [B][n_gen] and, if asked, the logits / layer
-    outputs seen at every step."""
+    outputs seen at every step.
+
+    With ``prefill_chunk``, each prompt goes through ``nq_prefill`` instead
+    (chunks of that many tokens), which yields its first generated token and
+    position; the remaining n_gen - 1 tokens come from decode steps. Logits and
+    layer outputs are then recorded for the decode steps only."""
+    if prefill_chunk:
+        return _run_prefilled(st, prompts, n_gen, use_graph, stream, record_logits, record_layers, prefill_chunk)
     B = st.batch
     P = [len(p) for p in prompts]
     total = max(P) + n_gen - 1
@@ -192,6 +225,40 @@ def run_greedy(st: Stepper, prompts, n_gen: int, use_graph: bool = False, stream
                 gen[b].append(int(nxt[b]))
             cur[b] = prompts[b][s + 1] if s + 1 < P[b] else nxt[b]
         st.set_tokens(cur)
+    st.check(stream)
+    out = {"tokens": np.array(gen, np.int64)}
+    if record_logits:
+        out["logits"] = np.array(logits)
+    if record_layers:
+        out["layer_out"] = np.array(layers)
+    return out
+
+
+def _run_prefilled(st: Stepper, prompts, n_gen, use_graph, stream, record_logits, record_layers, chunk):
+    B = st.batch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    pf = Prefill(st.model, st.kv, chunk)
+    for b in range(B):
+        pf.run(prompts[b], st.page_table[b], 0, next_token=st.tokens[b:b + 1], pos_out=st.pos[b:b + 1],
+               stream=stream)
+    pf.check(stream)
+    gen = [[int(t)] for t in st.tokens.cpu().numpy()]
+    logits, layers = [], []
+    if use_graph and st.graph is None:
+        st.capture(stream)
+    for _ in range(n_gen - 1):
+        if use_graph:
+            st.replay(stream)
+        else:
+            st.step(stream)
+        nxt = st.tokens.cpu().numpy()
+        if record_logits:
+            logits.append(st.logits.cpu().numpy().copy())
+        if record_layers:
+            layers.append(st.layer_out.cpu().numpy().copy())
+        for b in range(B):
+            gen[b].append(int(nxt[b]))
     st.check(stream)
     out = {"tokens": np.array(gen, np.int64)}
     if record_logits:

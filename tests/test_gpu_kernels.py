@@ -11,6 +11,13 @@ from gpu_util import F16, dev, host, rel_inf, say, exact_case_weights
 pytestmark = pytest.mark.gpu
 
 TOL_LAYER = 2e-3   # per-layer-output bar (infinity-norm relative)
+# fp32 outputs (no fp16 rounding at the end): the kernels accumulate the biased
+# fp16 codes (1024 + n, 16 * (72 + q)) against pre-scaled activations and
+# subtract the bias products in fp32, so a group's partial sum carries terms up
+# to ~1032 |x| before they cancel; with the unit roundoff 2^-24 that puts the
+# relative error at a few 1e-5 (measured 1.4e-5 at K = 512), against ~1e-7
+# for exact codes. The bar keeps a margin over that.
+TOL_F32 = 1e-4
 
 
 def _packed_dev(w, kind=nq.NQ_MAT_PLAIN, d=0):
@@ -87,7 +94,7 @@ def test_gemv_random_store_f16_and_f32(k, n, batch):
     assert rel_inf(host(y), ref.astype(F16)) < TOL_LAYER
     yf = torch.empty(batch, n, dtype=torch.float32, device="cuda")
     nq.nq_gemv_w4a16(p, n, k, 0, 0, batch, dev(x), None, 1e-6, None, yf, nq.NQ_EPI_STORE_F32)
-    assert rel_inf(host(yf), ref) < 1e-5
+    assert rel_inf(host(yf), ref) < TOL_F32
 
 
 @pytest.mark.parametrize("batch", [1, 4])

@@ -18,6 +18,7 @@ from gpu_util import F16, dev, host, rel_inf, say, exact_case_weights
 pytestmark = pytest.mark.gpu
 
 TOL_LAYER, TOL_LOGITS, MARGIN = 2e-3, 5e-3, 1e-2
+TOL_F32 = 1e-4     # fp32 outputs: see the note on biased codes in test_gpu_kernels.py
 
 
 def _pk(w, kind=nq.NQ_MAT_PLAIN, d=0):
@@ -58,7 +59,7 @@ def test_gemm_random_every_epilogue(m):
     assert rel_inf(host(y), ref.astype(F16)) < TOL_LAYER
     yf = torch.empty(m, 768, dtype=torch.float32, device="cuda")
     nq.nq_gemm_w4a16(p, 768, H, 0, 0, m, dev(x), None, yf, nq.NQ_EPI_STORE_F32)
-    assert rel_inf(host(yf), ref) < 1e-5
+    assert rel_inf(host(yf), ref) < TOL_F32
     nq.nq_gemm_w4a16(p, 768, H, 0, 0, m, dev(x), dev(b), y, nq.NQ_EPI_BIAS_F16)
     assert rel_inf(host(y), oracle.gemv_w4a16(qo, so, x, b).astype(F16)) < TOL_LAYER
     # residual, in place, on a K = 1408 (11 groups) matrix

@@ -34,25 +34,54 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One 32-bit word of eight offset-binary nibbles -> four pairs of exact fp16
-// codes: (q[k], q[k+1]), (q[k+2], q[k+3]), (q[k+4], q[k+5]), (q[k+6], q[k+7]).
-// A nibble n in bits 0-3 of a 16-bit half, OR'ed with 0x6400, is the half
-// 1024 + n; subtracting 1032 leaves q = n - 8 exactly. A nibble in bits 4-7
-// gives 1024 + 16n; (1024 + 16n) / 16 - 72 = n - 8, also exact. ``magic``
-// (0x64006400) is passed in a register so that each mask-and-insert is a
-// single v_and_or_b32 (gfx9 VOP3 cannot take two literal constants).
+// One 32-bit word of eight offset-binary nibbles n = q + 8 -> four pairs of
+// fp16 values, with no arithmetic: a nibble in bits 0-3 of a 16-bit half
+// OR'ed with 0x6400 is the half 1024 + n = q + 1032, a nibble in bits 4-7
+// gives 1024 + 16n = 16 (q + 72). Pairs 0 and 2 hold (q[k], q[k+1]) and
+// (q[k+4], q[k+5]) in the first form, pairs 1 and 3 hold (q[k+2], q[k+3]) and
+// (q[k+6], q[k+7]) in the second. ``magic`` (0x64006400) is passed in a
+// register so that each mask-and-insert is a single v_and_or_b32.
+//
+// The matrix-core products use these biased codes directly: the activations
+// are stored with the halves at K offsets 2, 3, 6, 7 (mod 8) multiplied by
+// 1/16 (exact for fp16 above the subnormal range), so that
+//   sum_k code_k x'_k = sum_k q_k x_k + sum_k bias_k x'_k,
+// bias_k = 1032 at offsets 0, 1, 4, 5 and 16 * 72 = 1152 at 2, 3, 6, 7; the
+// second term is removed by products with the constant fragment -bias. This
+// takes 5 VALU operations per word instead of 9, at the price of fp32
+// cancellation of the bias terms (a few 1e-5 relative on a group's sum).
+__device__ __forceinline__ void unpack8_biased(uint32_t w, uint32_t magic, h2 (&o)[4]) {
+  const uint32_t w8 = w >> 8;
+  o[0] = as_h2((w & 0x000F000Fu) | magic);
+  o[1] = as_h2((w & 0x00F000F0u) | magic);
+  o[2] = as_h2((w8 & 0x000F000Fu) | magic);
+  o[3] = as_h2((w8 & 0x00F000F0u) | magic);
+}
+
+// The exact codes from the biased ones: (q + 1032) - 1032 and 16 (q + 72) / 16 - 72.
 __device__ __forceinline__ void unpack8(uint32_t w, uint32_t magic, h2 (&o)[4]) {
   const h2 off_lo = {static_cast<half_t>(-1032.0f), static_cast<half_t>(-1032.0f)};
   const h2 sixteenth = {static_cast<half_t>(0.0625f), static_cast<half_t>(0.0625f)};
   const h2 off_hi = {static_cast<half_t>(-72.0f), static_cast<half_t>(-72.0f)};
-  const uint32_t w8 = w >> 8;
-  o[0] = as_h2((w & 0x000F000Fu) | magic) + off_lo;
-  o[1] = __builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | magic), sixteenth, off_hi);
-  o[2] = as_h2((w8 & 0x000F000Fu) | magic) + off_lo;
-  o[3] = __builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | magic), sixteenth, off_hi);
+  unpack8_biased(w, magic, o);
+  o[0] = o[0] + off_lo;
+  o[1] = __builtin_elementwise_fma(o[1], sixteenth, off_hi);
+  o[2] = o[2] + off_lo;
+  o[3] = __builtin_elementwise_fma(o[3], sixteenth, off_hi);
 }
 
 __device__ __forceinline__ void unpack8(uint32_t w, h2 (&o)[4]) { unpack8(w, 0x64006400u, o); }
+
+// Pre-scaling of 8 consecutive activations (K offsets 0..7 mod 8) for the
+// biased codes: halves 2, 3, 6, 7 times 1/16.
+__device__ __forceinline__ void scale_high_halves(uint32_t (&v)[4]) {
+  const h2 sixteenth = {static_cast<half_t>(0.0625f), static_cast<half_t>(0.0625f)};
+  v[1] = __builtin_bit_cast(uint32_t, as_h2(v[1]) * sixteenth);
+  v[3] = __builtin_bit_cast(uint32_t, as_h2(v[3]) * sixteenth);
+}
+
+// 1/16 for the K offsets (mod 8) that meet a high-nibble code, else 1.
+__device__ __forceinline__ float high_scale(int e) { return (e & 2) ? 0.0625f : 1.0f; }
 
 __device__ __forceinline__ float dot2(h2 a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(a, as_h2(b), c, false);
@@ -68,6 +97,13 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+
+// The constant MFMA A fragment -bias (every row alike; lane element i is K
+// offset 8*(lane/16) + i of the product, i.e. i mod 8 of the group's K).
+__device__ __forceinline__ half8 neg_bias_frag() {
+  const half_t a = static_cast<half_t>(-1032.0f), b = static_cast<half_t>(-1152.0f);
+  return half8{a, a, b, b, a, a, b, b};
+}
 
 constexpr int kBufferFlags = 0x00020000;    // gfx9 raw buffer descriptor word 3
 

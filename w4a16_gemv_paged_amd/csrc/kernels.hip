@@ -68,19 +68,27 @@ struct GemvParams {
   int32_t* err;
 };
 
-// Four 16x16x32 MFMAs over one (tile, group) block: d[i] = sum over the
-// group's 128 K of q[row 4*(l/16)+i][k] * x[col l%16][k] (unscaled).
-__device__ __forceinline__ f4 gemv_block_mfma(const u32x4& w, const half_t* xg, uint32_t magic) {
+// The 16x16x32 MFMAs over one (tile, group) block: d[i] = sum over the
+// group's 128 K of q[row 4*(l/16)+i][k] * x[col l%16][k] (unscaled), from the
+// biased codes: per K step one product with the constant -bias fragment (it
+// needs only x, so the first one goes ahead of the weights) and one with the
+// codes. The activations are pre-scaled in LDS when PRESCALED (the RMSNorm
+// pass does it for free), else here in registers.
+template <bool PRESCALED>
+__device__ __forceinline__ f4 gemv_block_mfma(const u32x4& w, const half_t* xg, uint32_t magic, const half8& nbias) {
   f4 d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
+    uint32_t xv[4];
+    *reinterpret_cast<u32x4*>(xv) = *reinterpret_cast<const u32x4*>(xg + j * 8);
+    if constexpr (!PRESCALED) scale_high_halves(xv);
+    const half8 xb = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(xv));
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(nbias, xb, d, 0, 0, 0);
     h2 q[4];
-    unpack8(w[j], magic, q);
+    unpack8_biased(w[j], magic, q);
     const u32x4 qa = {__builtin_bit_cast(uint32_t, q[0]), __builtin_bit_cast(uint32_t, q[1]),
                       __builtin_bit_cast(uint32_t, q[2]), __builtin_bit_cast(uint32_t, q[3])};
-    const u32x4 xb = *reinterpret_cast<const u32x4*>(xg + j * 8);
-    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, qa), __builtin_bit_cast(half8, xb), d,
-                                               0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, qa), xb, d, 0, 0, 0);
   }
   return d;
 }
@@ -104,6 +112,7 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
   float* ssq = red + nw * B * 16;                      // [nw][B]
   float* lg = ssq + nw * B;                            // [tpw][B][16]
   const uint32_t magic = opaque(0x64006400u);
+  const half8 nbias = neg_bias_frag();
   const int items = p.tpw * B * 16;
 
   // Inputs of the fused QKV epilogue (bias, position, RoPE cos/sin, page id)
@@ -227,8 +236,9 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * kDepth));  // this wave's LDS writes have landed
     __builtin_amdgcn_s_barrier();                     // ... and every wave's
     __builtin_amdgcn_sched_barrier(0);
-    // (3) x * gain in place, sum(x^2) (1/rms multiplies the outputs later);
-    //     workgroup 0 also stores the gathered embedding rows as the residual
+    // (3) x * gain in place, pre-scaled for the biased codes, and sum(x^2)
+    //     (1/rms multiplies the outputs later); workgroup 0 also stores the
+    //     gathered embedding rows as the residual
     if constexpr (GAIN) {
       for (int i = tid; i < B * n8; i += blockDim.x) {
         const int b = i / n8, j = i - b * n8;
@@ -243,7 +253,7 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
         for (int e = 0; e < 8; ++e) {
           const float f = static_cast<float>(hv[e]);
           sacc = fmaf(f, f, sacc);
-          hv[e] = static_cast<half_t>(f * static_cast<float>(gh[e]));
+          hv[e] = static_cast<half_t>(f * static_cast<float>(gh[e]) * high_scale(e));
         }
 #pragma unroll
         for (int bb = 0; bb < B; ++bb)
@@ -262,7 +272,7 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
       for (int u = 0; u < kDepth; ++u) {
         const int i = ib + u;
         if (i < n_c) {
-          const f4 d = gemv_block_mfma(wv[u], xlane + (ksi + p.ks * i) * xstep, magic);
+          const f4 d = gemv_block_mfma<GAIN>(wv[u], xlane + (ksi + p.ks * i) * xstep, magic, nbias);
           if (u > 0) scale_acc(acc, dprev, sprev);
           dprev = d;
           sprev = sv[u];
@@ -491,6 +501,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvPara
   float* ssq = part + p.tpw * cpt * B * 16;                  // [NW][B]
   float* lg = reinterpret_cast<float*>(smem);                // [tile][B][16], after the stream
   const uint32_t magic = opaque(0x64006400u);
+  const half8 nbias = neg_bias_frag();
 
   // the residual the epilogue adds to: one prefetched item per thread
   half_t e_res = static_cast<half_t>(0.0f);  // kept as loaded: converting it here would wait for it
@@ -561,7 +572,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvPara
 #pragma unroll
     for (int s2 = 0; s2 < CH; ++s2) {
       const int g = min(g0 + s2, g1 - 1);  // a zero slot reads a valid activation group
-      const f4 d = gemv_block_mfma(w[s2], xlane + g * xstep, magic);
+      const f4 d = gemv_block_mfma<GAIN>(w[s2], xlane + g * xstep, magic, nbias);
       scale_acc(acc, d, sc[s2]);
     }
     if (col < B) {
@@ -590,7 +601,8 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvPara
   load_chunk(qa, wa, sa);
   load_chunk(qb, wb, sb);
   __builtin_amdgcn_sched_barrier(0);
-  // (3) x * gain in place, and each wave's share of sum(x^2) per batch row
+  // (3) x * gain in place, pre-scaled for the biased codes, and each wave's
+  //     share of sum(x^2) per batch row
   if constexpr (GAIN) {
     const int n8 = G * 16;
     for (int b = 0; b < B; ++b) {
@@ -604,7 +616,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvPara
         for (int e = 0; e < 8; ++e) {
           const float f = static_cast<float>(hv[e]);
           sacc = fmaf(f, f, sacc);
-          hv[e] = static_cast<half_t>(f * static_cast<float>(gh[e]));
+          hv[e] = static_cast<half_t>(f * static_cast<float>(gh[e]) * high_scale(e));
         }
         *reinterpret_cast<uint4*>(xs + b * xrow + j * 8) = v;
       }

@@ -116,6 +116,28 @@ __device__ __forceinline__ void scale_acc(f4& acc, const f4& d, const u32x2& sc)
   acc[3] = fmaf(d[3], static_cast<float>(s23[1]), acc[3]);
 }
 
+// Lane n of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x150 + N, 0xF, 0xF, false));
+}
+
+// The same for both words of a pair; n must be a constant once the caller's
+// loop is unrolled (the switch then folds away).
+__device__ __forceinline__ u32x2 row_bcast2(const u32x2& v, int n) {
+  switch (n & 15) {
+#define NQ_BCAST_CASE(N) \
+  case N:                \
+    return u32x2{row_bcast<N>(v.x), row_bcast<N>(v.y)};
+    NQ_BCAST_CASE(0) NQ_BCAST_CASE(1) NQ_BCAST_CASE(2) NQ_BCAST_CASE(3)
+    NQ_BCAST_CASE(4) NQ_BCAST_CASE(5) NQ_BCAST_CASE(6) NQ_BCAST_CASE(7)
+    NQ_BCAST_CASE(8) NQ_BCAST_CASE(9) NQ_BCAST_CASE(10) NQ_BCAST_CASE(11)
+    NQ_BCAST_CASE(12) NQ_BCAST_CASE(13) NQ_BCAST_CASE(14) NQ_BCAST_CASE(15)
+#undef NQ_BCAST_CASE
+  }
+  return v;
+}
+
 // Greedy tie rule: larger value wins, equal values go to the lower index.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 

@@ -35,7 +35,7 @@ namespace nq {
 // row are scaled by that row's fp16 group scale in fp32. Slices of a tile are
 // summed through LDS, then the fused epilogue runs on (tile, batch, row) items.
 
-constexpr int kDepth = 8;                   // 1 KiB weight loads in flight per wave
+constexpr int kDepth = 7;                   // 1 KiB weight loads in flight per wave
 constexpr int kDmaBatch = 8;                // activation copies issued back to back per wave
 constexpr size_t kLdsX = 56 * 1024;         // LDS budget for staged activations and gain
 
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
       const_cast<uint8_t*>(p.codes) + static_cast<size_t>(tq) * p.G * kBlockBytes, 0, wbytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.scales) + static_cast<size_t>(tq) * p.G * 32, 0, sbytes, kBufferFlags);
-  const int wvoff = lane * 16, svoff = kb * 8;
+  const int wvoff = lane * 16;
   // B fragment of this lane: its batch row, or the zero block for columns >= B
   const half_t* xlane = (col < B ? xs + col * xrow : zero) + kb * 32;
   const int xstep = col < B ? 128 : 0;
@@ -178,7 +178,6 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
   }
 
   u32x4 wv[kDepth];
-  u32x2 sv[kDepth];
   f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   float ss[B];
 #pragma unroll
@@ -223,17 +222,26 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // (2) The weight ring: exactly 2 * kDepth loads per wave (absent groups
-    //     read past the tile and return 0), so the wait below is exact.
+    // (2) The scale window of the first kDepth blocks and the weight ring:
+    //     exactly kDepth + 1 loads per wave (absent groups read past the tile
+    //     and return 0), so the wait below is exact. In a scale window, lane
+    //     (row kb, column c < kDepth) holds the scales of rows 4kb..4kb+3 for
+    //     block w0 + c; block i takes them from lane i % kDepth of its row. One
+    //     64-lane load thus serves kDepth blocks instead of one.
+    auto load_scales = [&](int w0) {
+      const int bi = w0 + col;
+      const int g = c0 + ksi + p.ks * bi;
+      return __builtin_amdgcn_raw_buffer_load_b64(srs, (col < kDepth && bi < n_c) ? g * 32 + kb * 8 : sbytes, 0, 0);
+    };
+    u32x2 swin = load_scales(0);
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
       const bool ok = u < n_c;
       const int g = c0 + ksi + p.ks * u;
       wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff, ok ? g * kBlockBytes : wbytes, 0);
-      sv[u] = __builtin_amdgcn_raw_buffer_load_b64(srs, svoff, ok ? g * 32 : sbytes, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * kDepth));  // this wave's LDS writes have landed
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kDepth + 1));  // this wave's LDS writes have landed
     __builtin_amdgcn_s_barrier();                     // ... and every wave's
     __builtin_amdgcn_sched_barrier(0);
     // (3) x * gain in place, pre-scaled for the biased codes, and sum(x^2)
@@ -264,8 +272,10 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
-    // (4) the scale of group i is applied while group i+1 is on the matrix cores
+    // (4) the scale of block i is applied while block i+1 is on the matrix
+    //     cores; the next scale window is requested a window ahead
     for (int ib = 0; ib < n_c; ib += kDepth) {
+      const u32x2 snext = load_scales(ib + kDepth);
       f4 dprev;
       u32x2 sprev;
 #pragma unroll
@@ -275,15 +285,15 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
           const f4 d = gemv_block_mfma<GAIN>(wv[u], xlane + (ksi + p.ks * i) * xstep, magic, nbias);
           if (u > 0) scale_acc(acc, dprev, sprev);
           dprev = d;
-          sprev = sv[u];
+          sprev = row_bcast2(swin, u);
           if (i + kDepth < n_c) {  // refill the slot just consumed
             const int gn = c0 + ksi + p.ks * (i + kDepth);
             wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff, gn * kBlockBytes, 0);
-            sv[u] = __builtin_amdgcn_raw_buffer_load_b64(srs, svoff, gn * 32, 0);
           }
         }
       }
       scale_acc(acc, dprev, sprev);
+      swin = snext;
     }
   };
   if (p.ch >= p.G) {
@@ -518,7 +528,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvPara
       const_cast<uint8_t*>(p.codes) + static_cast<size_t>(t0) * G * kBlockBytes, 0, nb * kBlockBytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.scales) + static_cast<size_t>(t0) * G * 32, 0, nb * 32, kBufferFlags);
-  const int wvoff = lane * 16, svoff = kb * 8;
+  const int wvoff = lane * 16;
   const half_t* xlane = (col < B ? xs + col * xrow : zero) + kb * 32;
   const int xstep = col < B ? 128 : 0;
   if (tid < 16) reinterpret_cast<uint4*>(zero)[tid] = make_uint4(0u, 0u, 0u, 0u);
@@ -554,18 +564,21 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvPara
     g0 = c * G / cpt;
     g1 = (c + 1) * G / cpt;
   };
-  auto load_chunk = [&](int q, u32x4 (&w)[CH], u32x2 (&sc)[CH]) {
+  // The chunk's scales come in one 64-lane load: lane (row kb, column c < CH)
+  // holds rows 4kb..4kb+3 of slot c; slot s2 takes them from lane s2 of its row.
+  auto load_chunk = [&](int q, u32x4 (&w)[CH], u32x2& sc) {
     int g0, g1, j;
     chunk_range(q, g0, g1, j);
     const bool in = q < Q;
+    const int fs = (in && col < CH && g0 + col < g1) ? j * G + g0 + col : nb;
+    sc = __builtin_amdgcn_raw_buffer_load_b64(srs, fs * 32 + kb * 8, 0, 0);
 #pragma unroll
     for (int s2 = 0; s2 < CH; ++s2) {
       const int f = (in && g0 + s2 < g1) ? j * G + g0 + s2 : nb;   // nb: out of range, reads 0
       w[s2] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff, f * kBlockBytes, 0);
-      sc[s2] = __builtin_amdgcn_raw_buffer_load_b64(srs, svoff, f * 32, 0);
     }
   };
-  auto compute_chunk = [&](int q, const u32x4 (&w)[CH], const u32x2 (&sc)[CH]) {
+  auto compute_chunk = [&](int q, const u32x4 (&w)[CH], const u32x2& sc) {
     int g0, g1, j;
     chunk_range(q, g0, g1, j);
     f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -573,7 +586,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvPara
     for (int s2 = 0; s2 < CH; ++s2) {
       const int g = min(g0 + s2, g1 - 1);  // a zero slot reads a valid activation group
       const f4 d = gemv_block_mfma<GAIN>(w[s2], xlane + g * xstep, magic, nbias);
-      scale_acc(acc, d, sc[s2]);
+      scale_acc(acc, d, row_bcast2(sc, s2));
     }
     if (col < B) {
 #pragma unroll
@@ -595,7 +608,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvPara
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   u32x4 wa[CH], wb[CH];
-  u32x2 sa[CH], sb[CH];
+  u32x2 sa, sb;
   int qa = wave;
   int qb = NW + wave;
   load_chunk(qa, wa, sa);

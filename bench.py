@@ -4,8 +4,9 @@ with symmetric group-128 INT4 weights (fp16 scales) and fp16 activations,
 random-init (synthetic) weights and prompts.
 
 Headline (the printed JSON line): batch-1 greedy decode, 512-token random
-prompt fed through the step, then the step replayed as one HIP graph per token;
-``value`` = tokens/s over exactly --steps timed replays (after --warmup).
+prompt fed through the chunked prefill (timed: the time to first token), then
+the step replayed as one HIP graph per token; ``value`` = tokens/s over exactly
+--steps timed replays (after --warmup).
 The same line also carries the batch-8 decode (ragged contexts uniform in
 [128, 16384], 128 steps), the W4A16 GEMV sweep at the 7B projection shapes
 (GB/s and fraction of the 8 TB/s HBM peak), the roofline of the dominant
@@ -99,6 +100,27 @@ def time_launches(fn, launches: int, stream, reps: int = 1):
     e1.record(stream)
     stream.synchronize()
     return sum(per) / len(per), e0.elapsed_time(e1) * 1e-3 / (launches * reps)
+
+
+PEAK_MFMA_F16 = 2.5e15   # MI355X dense fp16 matrix peak
+
+
+def ttft_block(shape, prompt: int, ms: float, ms_per_token: float) -> dict:
+    """Time to first token of the chunked prefill (one chunk of ``prompt`` rows)
+    beside feeding the same prompt through the decode step one token at a time.
+    The projections of a prompt row cost 2 flops per weight; the attention adds
+    4 * d flops per (query head, earlier position) pair."""
+    H, I, nh, nkv, d = shape.hidden, shape.intermediate, shape.n_heads, shape.n_kv_heads, shape.head_dim
+    weights = H * (nh + 2 * nkv) * d + nh * d * H + 2 * H * I + I * H
+    gemm_flop = 2 * weights * prompt * shape.layers
+    attn_flop = 4 * d * nh * shape.layers * prompt * (prompt + 1) / 2
+    return {"prompt_tokens": prompt, "chunk": prompt, "ms": round(ms, 3),
+            "prefill_tok_s": round(prompt / ms * 1e3, 1),
+            "kernels": 7 * shape.layers + 2,
+            "flop": int(gemm_flop + attn_flop),
+            "tflops": round((gemm_flop + attn_flop) / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round((gemm_flop + attn_flop) / (ms * 1e-3) / PEAK_MFMA_F16, 4),
+            "token_by_token_ms": round(prompt * ms_per_token, 2)}
 
 
 def gate_up_roofline(layers, hidden: int, inter: int, stream, reps: int = 10):
@@ -245,7 +267,7 @@ def main() -> int:
     import torch
     import synth
     import w4a16_gemv_paged_amd as nq
-    from w4a16_gemv_paged_amd.engine import DeviceModel, KVCache, Stepper
+    from w4a16_gemv_paged_amd.engine import DeviceModel, KVCache, Stepper, Prefill
 
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
@@ -292,14 +314,25 @@ def main() -> int:
     kv1 = KVCache(dm, total, poison=False)
     st = Stepper(dm, kv1, pt, hist_len=need + 1)
     with torch.cuda.stream(stream):
-        st.set_pos([0])
-        st.set_tokens([prompt[0]])
+        # time to first token: the prompt through the chunked prefill (one chunk of
+        # P rows), which leaves the first generated token and its position in the
+        # step's device buffers; timed over a few repeats on the same pages
+        pf = Prefill(dm, kv1, P)
+        row = st.page_table[0]
+        ttft = []
+        for r in range(6):
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ea.record(stream)
+            pf.run(prompt, row, 0, next_token=st.tokens[0:1], pos_out=st.pos[0:1], stream=stream)
+            eb.record(stream)
+            torch.cuda.synchronize()
+            if r > 0:
+                ttft.append(ea.elapsed_time(eb))
+        pf.check(stream)
+        ttft_ms = float(np.median(ttft))
+        del pf
         n_kernels = st.capture(stream)
-        log(f"captured the step: {n_kernels} kernels")
-        for i in range(P):                      # prompt, one token per replay
-            st.replay(stream)
-            if i + 1 < P:
-                st.set_tokens([prompt[i + 1]])
+        log(f"prefill of {P} tokens (TTFT): {ttft_ms:.2f} ms; captured the step: {n_kernels} kernels")
         for _ in range(W):
             st.replay(stream)
         torch.cuda.synchronize()
@@ -325,7 +358,7 @@ def main() -> int:
         ms_eager = (time.perf_counter() - t2) * 1e3 / ne
         st.check(stream)
     hist = st.hist.cpu().numpy()[0]
-    gen = hist[P:P + W + K]
+    gen = hist[P + 1:P + 1 + W + K]
     log(f"B=1: {ms_b1:.3f} ms/token ({1e3 / ms_b1:.1f} tok/s), eager {ms_eager:.3f} ms/token; "
         f"first tokens {gen[:8].tolist()}")
     st.close()
@@ -407,6 +440,7 @@ def main() -> int:
         "step_roofline_ms": round(wb / PEAK_HBM * 1e3, 4),
         "step_roofline_frac": round(wb / PEAK_HBM * 1e3 / ms_b1, 4),
         "dominant_kernel": roof,
+        "ttft": ttft_block(shape, P, ttft_ms, ms_b1),
         "b8": b8,
         "gemv_sweep": sweep, "gemv_aggregate": agg,
         "context": {"pages_h100_ms_per_token_graph": 16.7, "pages_h100_ms_per_token_eager": 119,

@@ -15,6 +15,9 @@ Qwen2.5-Coder-7B-class model):
   greedy-only sampling.
 * "How To Build Your Own LLM Runtime From Scratch" (daily.dev), Summary and
   FAQ: 28 layers, FP16 activations with INT4 weights, partial KV tail pages.
+* "How To Build Your Own LLM Runtime From Scratch" (daily.dev), FAQ on
+  INT8-activation dp4a against FP16-activation INT4 unpack: the INT8
+  activation variant (``a8.py``).
 * "Inference Zero To Hero" (preface), the stable softmax shown under "How
   each chapter works": subtract the max, exponentiate, divide by the sum.
 * "Build Crude Implementations for Learning", section "nanoGPT level":
@@ -29,6 +32,7 @@ Parity status: every function here is pinned by tests in
 "parity unpinned".
 """
 from .quant import quantize_w4, dequantize_w4, GROUP
+from .a8 import quantize_a8, dequantize_a8, gemv_w4a8
 from .model import (
     softmax, rmsnorm, rope, attend, attend_splitk, swiglu, argmax_lowest,
     ContiguousKV, PagedKVEmu, OracleModel, layer_causal, causal_forward,
@@ -36,7 +40,7 @@ from .model import (
 )
 
 __all__ = [
-    "quantize_w4", "dequantize_w4", "GROUP", "softmax", "rmsnorm", "rope",
+    "quantize_w4", "dequantize_w4", "GROUP", "quantize_a8", "dequantize_a8", "gemv_w4a8", "softmax", "rmsnorm", "rope",
     "attend", "attend_splitk", "swiglu", "argmax_lowest", "ContiguousKV",
     "PagedKVEmu", "OracleModel", "layer_causal", "causal_forward",
     "decode_step", "generate", "gemv_w4a16", "paged_attention",

@@ -183,6 +183,43 @@ nq_status nq_gemm_w4a16(const void* packed, int32_t N, int32_t K, nq_mat_kind ki
                         int32_t head_dim, int32_t M, const void* x, const void* bias,
                         void* y, nq_epilogue epi, void* stream);
 
+/* ------------------------------------------------------------- W4A8 variant */
+
+/*
+ * INT8-activation variant of the projections ("How To Build Your Own LLM
+ * Runtime From Scratch" (daily.dev), Summary and the FAQ question on
+ * INT8-activation dp4a against FP16-activation INT4 unpack: the activations
+ * are quantised to INT8 before the GEMV and multiplied with the INT4 weights in
+ * integer arithmetic). The pages give no quantisation rule; this library uses
+ * one scale per row and group of 128 inputs:
+ *   s = fp32(max |x| over the group) / 127,
+ *   q = clamp(round_half_even(fp32(x) / s), -127, 127)   (q = 0 when s = 0),
+ * the group's integer sum of q_w * q multiplied by the fp16 weight scale and s
+ * in fp32. Batch 1..4.
+ *
+ * Quantised activations of `batch` rows of K inputs take nq_a8_bytes(batch, K)
+ * device bytes: batch*K int8 codes (each 8 inputs k0..k0+7 stored in the order
+ * k0, k0+4, k0+1, k0+5, k0+2, k0+6, k0+3, k0+7), then per (row, group) a float
+ * scale and the int32 sum of the group's codes, padded to 16 bytes.
+ */
+size_t nq_a8_bytes(int32_t batch, int32_t K);
+
+/* Quantise fp16 x [batch][K] (device) into xq (device, nq_a8_bytes bytes,
+ * 16-byte aligned). Errors: NQ_ERR_INVALID_ARG (null/misaligned pointers,
+ * K % 128, batch outside 1..4). */
+nq_status nq_quantize_a8(const void* x, int32_t batch, int32_t K, void* xq, void* stream);
+
+/* y = W x with INT8 activations. xq non-NULL: the activations quantised by
+ * nq_quantize_a8 (x is ignored); xq NULL: the kernel quantises fp16 x itself
+ * in its prologue, which needs all of K of the batch in LDS
+ * (NQ_ERR_UNSUPPORTED otherwise; quantise first then). The same arithmetic
+ * either way, bit for bit. packed, kind, head_dim, bias, y and epi as
+ * nq_gemv_w4a16 (no RMSNorm prologue; epilogues STORE_F16, BIAS_F16,
+ * RESIDUAL_F16, SWIGLU_F16, STORE_F32). */
+nq_status nq_gemv_w4a8(const void* packed, int32_t N, int32_t K, nq_mat_kind kind,
+                       int32_t head_dim, int32_t batch, const void* x, const void* xq,
+                       const void* bias, void* y, nq_epilogue epi, void* stream);
+
 /* ------------------------------------------------------------ model config */
 
 typedef struct nq_config {

@@ -27,6 +27,7 @@ __all__ = [
     "nq_model_bind_workspace", "nq_model_destroy", "nq_decode_step", "nq_graph_capture",
     "nq_graph_launch", "nq_graph_kernel_count", "nq_graph_destroy", "nq_check_device_error",
     "nq_gemm_w4a16", "nq_attn_prefill", "NQPrefillIO", "nq_prefill_workspace_bytes", "nq_prefill",
+    "nq_a8_bytes", "nq_quantize_a8", "nq_gemv_w4a8",
     "header_symbols",
 ]
 
@@ -122,6 +123,9 @@ _SIGS = {
     "nq_attn_prefill": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P, _P]),
     "nq_prefill_workspace_bytes": (_S, [_CFG, _I]),
     "nq_prefill": (_I, [_P, _P, ctypes.POINTER(NQPrefillIO), _P]),
+    "nq_a8_bytes": (_S, [_I, _I]),
+    "nq_quantize_a8": (_I, [_P, _I, _I, _P, _P]),
+    "nq_gemv_w4a8": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P]),
 }
 
 _lib = None
@@ -231,6 +235,19 @@ def nq_gemv_w4a16(packed, N, K, kind, head_dim, batch, x, norm_gain, eps, bias, 
 def nq_gemm_w4a16(packed, N, K, kind, head_dim, M, x, bias, y, epi, stream=None):
     _check(lib().nq_gemm_w4a16(_ptr(packed), N, K, kind, head_dim, M, _ptr(x), _ptr(bias), _ptr(y), epi,
                                _stream(stream)), "nq_gemm_w4a16")
+
+
+def nq_a8_bytes(batch: int, K: int) -> int:
+    return lib().nq_a8_bytes(batch, K)
+
+
+def nq_quantize_a8(x, batch, K, xq, stream=None):
+    _check(lib().nq_quantize_a8(_ptr(x), batch, K, _ptr(xq), _stream(stream)), "nq_quantize_a8")
+
+
+def nq_gemv_w4a8(packed, N, K, kind, head_dim, batch, x, xq, bias, y, epi, stream=None):
+    _check(lib().nq_gemv_w4a8(_ptr(packed), N, K, kind, head_dim, batch, _ptr(x), _ptr(xq), _ptr(bias), _ptr(y),
+                              epi, _stream(stream)), "nq_gemv_w4a8")
 
 
 def nq_config_check(cfg: NQConfig) -> None:

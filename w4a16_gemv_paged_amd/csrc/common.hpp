@@ -165,6 +165,18 @@ struct PrefillAttnArgs {
 };
 hipError_t launch_attn_prefill(const PrefillAttnArgs& a, hipStream_t s);
 
+// ------------------------------------------------------------ W4A8 variant
+
+// Bytes of the INT8 activations of `batch` rows of K inputs: the codes, then
+// the (float scale, int32 code sum) pairs of every (row, group), padded to 16.
+size_t a8_buffer_bytes(int32_t batch, int32_t K);
+hipError_t launch_quantize_a8(const void* x, int32_t batch, int32_t K, void* xq, hipStream_t s);
+// Whether the GEMV can quantise its own activations (all of K in LDS).
+bool a8_fused_fits(int32_t N, int32_t K, int32_t batch);
+// xq == nullptr: quantise x in the prologue; else read the quantised xq.
+hipError_t launch_gemv_w4a8(const void* packed, int32_t N, int32_t K, int32_t kind, int32_t head_dim, int32_t batch,
+                            const void* x, const void* xq, const void* bias, void* y, int epi, hipStream_t s);
+
 hipError_t launch_unpack_dev(const void* packed, int32_t N, int32_t K, int32_t kind,
                              int32_t head_dim, int8_t* q_out, uint16_t* s_out, hipStream_t s);
 

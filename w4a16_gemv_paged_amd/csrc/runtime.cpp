@@ -484,6 +484,46 @@ nq_status nq_gemm_w4a16(const void* packed, int32_t N, int32_t K, nq_mat_kind ki
   return NQ_OK;
 }
 
+size_t nq_a8_bytes(int32_t batch, int32_t K) {
+  if (batch < 1 || batch > 4 || K <= 0 || K % kGroup != 0) return 0;
+  return a8_buffer_bytes(batch, K);
+}
+
+nq_status nq_quantize_a8(const void* x, int32_t batch, int32_t K, void* xq, void* stream) {
+  if (!x || !xq) return fail(NQ_ERR_INVALID_ARG, "nq_quantize_a8: null x or xq");
+  if (!aligned16(x) || !aligned16(xq)) return fail(NQ_ERR_INVALID_ARG, "x and xq must be 16-byte aligned");
+  if (batch < 1 || batch > 4) return fail(NQ_ERR_INVALID_ARG, "batch %d outside 1..4", batch);
+  if (K <= 0 || K % kGroup != 0) return fail(NQ_ERR_INVALID_ARG, "K must be a positive multiple of 128");
+  hipError_t e = launch_quantize_a8(x, batch, K, xq, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "nq_quantize_a8 launch");
+  return NQ_OK;
+}
+
+nq_status nq_gemv_w4a8(const void* packed, int32_t N, int32_t K, nq_mat_kind kind, int32_t head_dim, int32_t batch,
+                       const void* x, const void* xq, const void* bias, void* y, nq_epilogue epi, void* stream) {
+  nq_status st = check_pack_args(N, K, kGroup, kind, head_dim);
+  if (st != NQ_OK) return st;
+  if (!packed || !y || (!x && !xq)) return fail(NQ_ERR_INVALID_ARG, "nq_gemv_w4a8: null packed, y, or both x and xq");
+  if (!aligned16(packed) || (x && !aligned16(x)) || (xq && !aligned16(xq)))
+    return fail(NQ_ERR_INVALID_ARG, "nq_gemv_w4a8: packed, x and xq must be 16-byte aligned");
+  if (batch < 1 || batch > 4) return fail(NQ_ERR_INVALID_ARG, "batch %d outside 1..4", batch);
+  if (epi < NQ_EPI_STORE_F16 || epi > NQ_EPI_STORE_F32)
+    return fail(NQ_ERR_INVALID_ARG, "unknown epilogue %d", static_cast<int>(epi));
+  if (epi == NQ_EPI_SWIGLU_F16 && kind != NQ_MAT_GATE_UP)
+    return fail(NQ_ERR_INVALID_ARG, "SwiGLU epilogue needs a GATE_UP matrix");
+  if (epi != NQ_EPI_SWIGLU_F16 && kind == NQ_MAT_GATE_UP)
+    return fail(NQ_ERR_INVALID_ARG, "a GATE_UP matrix needs the SwiGLU epilogue");
+  if (epi == NQ_EPI_BIAS_F16 && !bias) return fail(NQ_ERR_INVALID_ARG, "bias epilogue needs bias");
+  if (!xq && !a8_fused_fits(N, K, batch))
+    return fail(NQ_ERR_UNSUPPORTED, "K=%d at batch %d does not fit LDS for in-kernel quantisation; "
+                                     "quantise with nq_quantize_a8 first", K, batch);
+  hipError_t e = launch_gemv_w4a8(packed, N, K, kind, head_dim, batch, x, xq, bias, y, epi,
+                                  static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return fail(NQ_ERR_UNSUPPORTED, "nq_gemv_w4a8: shape does not fit LDS");
+  if (e != hipSuccess) return hip_fail(e, "nq_gemv_w4a8 launch");
+  return NQ_OK;
+}
+
 nq_status nq_unpack_weights_dev(const void* packed_dev, int32_t N, int32_t K, int32_t group,
                                 nq_mat_kind kind, int32_t head_dim, int8_t* q_out_dev, uint16_t* s_out_dev,
                                 void* stream) {

@@ -9,7 +9,9 @@ the step replayed as one HIP graph per token; ``value`` = tokens/s over exactly
 --steps timed replays (after --warmup).
 The same line also carries the batch-8 decode (ragged contexts uniform in
 [128, 16384], 128 steps), the W4A16 GEMV sweep at the 7B projection shapes
-(GB/s and fraction of the 8 TB/s HBM peak), the roofline of the dominant
+(GB/s and fraction of the 8 TB/s HBM peak; beside each, the INT8-activation
+variant with its quantisation fused into the GEMV and as a separate kernel),
+the roofline of the dominant
 kernel (the gate/up GEMV + SwiGLU) and the CPU oracle timed on a bounded
 sample.
 
@@ -174,10 +176,29 @@ def gemv_sweep(stream):
                 fn(j)
             mean_s, b2b_s = time_launches(fn, copies, stream, reps=max(1, 256 // copies))
             nb = gemv_bytes(k, n, b)
-            out.append({"K": k, "N": n, "B": b, "bytes": nb, "us": round(b2b_s * 1e6, 2),
-                        "GBs": round(nb / b2b_s / 1e9, 1), "frac": round(nb / b2b_s / PEAK_HBM, 4),
-                        "event_pair_us": round(mean_s * 1e6, 2)})
-            log(f"gemv K={k} N={n} B={b}: {b2b_s * 1e6:.2f} us {nb / b2b_s / 1e9:.0f} GB/s")
+            row = {"K": k, "N": n, "B": b, "bytes": nb, "us": round(b2b_s * 1e6, 2),
+                   "GBs": round(nb / b2b_s / 1e9, 1), "frac": round(nb / b2b_s / PEAK_HBM, 4),
+                   "event_pair_us": round(mean_s * 1e6, 2)}
+            # the INT8-activation variant on the same weights: a separate quantise
+            # kernel before each GEMV, and quantisation in the GEMV prologue
+            xq = torch.empty(nq.nq_a8_bytes(b, k), dtype=torch.uint8, device="cuda")
+            yf = torch.empty(b, n, dtype=torch.float16, device="cuda")
+            fq = lambda j: nq.nq_quantize_a8(x, b, k, xq, sid)
+            f2 = lambda j: (nq.nq_quantize_a8(x, b, k, xq, sid),
+                            nq.nq_gemv_w4a8(bufs[j], n, k, 0, 0, b, x, xq, None, yf, 0, sid))
+            reps = max(1, 256 // copies)
+            row["w4a8_quantize_us"] = round(time_launches(fq, copies, stream, reps=reps)[1] * 1e6, 2)
+            row["w4a8_two_kernels_us"] = round(time_launches(f2, copies, stream, reps=reps)[1] * 1e6, 2)
+            row["w4a8_fused_us"] = None
+            try:
+                ff = lambda j: nq.nq_gemv_w4a8(bufs[j], n, k, 0, 0, b, x, None, None, yf, 0, sid)
+                ff(0)
+                row["w4a8_fused_us"] = round(time_launches(ff, copies, stream, reps=reps)[1] * 1e6, 2)
+            except nq.NQError:
+                pass   # the batch's K does not fit LDS for in-kernel quantisation
+            out.append(row)
+            log(f"gemv K={k} N={n} B={b}: {b2b_s * 1e6:.2f} us {nb / b2b_s / 1e9:.0f} GB/s; W4A8 fused "
+                f"{row['w4a8_fused_us']} us, quantise + W4A8 {row['w4a8_two_kernels_us']} us")
         del bufs
     agg = {}
     for b in (1, 4):

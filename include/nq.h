@@ -49,7 +49,9 @@ typedef enum nq_status {
   NQ_ERR_OUT_OF_RANGE = 3,  /* value outside representable / configured range  */
   NQ_ERR_HIP = 4,           /* a HIP runtime call failed (message has details) */
   NQ_ERR_STATE = 5,         /* call not allowed in the current state           */
-  NQ_ERR_DEVICE_FAULT = 6   /* a kernel flagged a range error (err_flag != 0)  */
+  NQ_ERR_DEVICE_FAULT = 6,  /* a kernel flagged a range error (err_flag != 0)  */
+  NQ_ERR_IO = 7             /* a file could not be read, written or mapped, or
+                               is not a valid packed-weight container          */
 } nq_status;
 
 /* Name of a status code ("NQ_OK", ...). Never NULL. */
@@ -240,6 +242,67 @@ typedef struct nq_config {
 
 /* Checks a configuration; NQ_OK or NQ_ERR_INVALID_ARG / NQ_ERR_UNSUPPORTED. */
 nq_status nq_config_check(const nq_config* cfg);
+
+/* -------------------------------------------------- packed-weight container */
+
+/*
+ * One file holding a model's configuration and its tensors, with the
+ * projections already in the packed tile layout, written once offline and
+ * memory-mapped at load so that loading does no repacking ("How to build your
+ * own LLM runtime from scratch", "What it actually builds": the INT4 weights
+ * live in a memory-mapped binary file with a magic-byte header).
+ *
+ * Format version 1 (little-endian): a 4096-byte header (magic "NQPACKW4",
+ * format version, the packed tile layout version of nq_layout_version, the
+ * model configuration without max_batch / max_pos, the tensor count and the
+ * position of the tensor table, an FNV-1a 64 checksum of the header); the
+ * tensors, each at a 4096-byte aligned offset; the tensor table (per tensor:
+ * a NUL-terminated name of at most 47 bytes, role, matrix kind, shape, offset,
+ * size and the FNV-1a 64 checksum of its bytes). Opening checks the magic,
+ * versions, header checksum and that every record is consistent and inside the
+ * file; nq_container_verify also checks the tensor checksums.
+ */
+typedef enum nq_tensor_role {
+  NQ_TENSOR_PACKED = 1,  /* nq_pack_weights output of an N x K matrix of kind mat_kind */
+  NQ_TENSOR_F16 = 2      /* fp16 [N][K] (a vector has K = 1)                          */
+} nq_tensor_role;
+
+typedef struct nq_tensor_desc {
+  char name[48];
+  int32_t role;       /* nq_tensor_role                                */
+  int32_t mat_kind;   /* NQ_TENSOR_PACKED: nq_mat_kind                 */
+  int32_t N, K;
+  int32_t head_dim;   /* NQ_TENSOR_PACKED of kind QKV                  */
+  uint64_t bytes;     /* nq_packed_size(N, K, 128) or N * K * 2        */
+} nq_tensor_desc;
+
+typedef struct nq_container_writer nq_container_writer;
+typedef struct nq_container nq_container;
+
+/* Streaming writer: create, add exactly n_tensors tensors (host memory), finish.
+ * Errors: NQ_ERR_INVALID_ARG (bad config, name, duplicate, size that does not
+ * match role and shape), NQ_ERR_IO (file errors), NQ_ERR_STATE (count).
+ * nq_container_finish frees the writer whatever it returns. */
+nq_status nq_container_create(const char* path, const nq_config* cfg, int32_t n_tensors,
+                              nq_container_writer** out);
+nq_status nq_container_add(nq_container_writer* w, const nq_tensor_desc* desc, const void* data);
+nq_status nq_container_finish(nq_container_writer* w);
+
+/* Maps a container read-only. Errors: NQ_ERR_IO (missing, truncated or invalid
+ * file, other layout version). */
+nq_status nq_container_open(const char* path, nq_container** out);
+/* The stored configuration (max_batch and max_pos set to 1: runtime choices). */
+nq_status nq_container_config(const nq_container* c, nq_config* out);
+int32_t nq_container_count(const nq_container* c);
+/* Description and host pointer (into the mapping, valid until close) of a
+ * tensor by name or by index. NQ_ERR_OUT_OF_RANGE if there is none. */
+nq_status nq_container_tensor(const nq_container* c, const char* name, nq_tensor_desc* desc,
+                              const void** data);
+nq_status nq_container_tensor_at(const nq_container* c, int32_t index, nq_tensor_desc* desc,
+                                 const void** data);
+/* Recomputes every tensor checksum (reads the whole file). NQ_ERR_IO on a mismatch. */
+nq_status nq_container_verify(const nq_container* c);
+void nq_container_close(nq_container* c);
 
 /* ---------------------------------------------------------------- KV cache */
 

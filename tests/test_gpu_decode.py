@@ -9,7 +9,7 @@ import torch
 import oracle
 import synth
 from oracle.model import OracleModel, layer_causal, head_logits
-from w4a16_gemv_paged_amd.engine import DeviceModel, KVCache, Stepper, run_greedy
+from w4a16_gemv_paged_amd.engine import DeviceModel, KVCache, Stepper, run_greedy, write_container
 from gpu_util import F16, rel_inf, say
 
 pytestmark = pytest.mark.gpu
@@ -216,3 +216,19 @@ def test_split_attention_batch8(tiny):
     g = _run(dm, prompts, 3, pages=64, graph=True, layers=False)
     assert g["kernels"] == 6 * SHAPE.layers + 2
     np.testing.assert_array_equal(g["logits"].view(np.uint32), gpu["logits"].view(np.uint32))
+
+
+def test_model_from_container_decodes_identically(tiny, tmp_path):
+    """The same weights through the packed-weight container (written once,
+    memory-mapped and uploaded without repacking) decode bit for bit alike."""
+    om, dm = tiny
+    path = str(tmp_path / "tiny.nqpack")
+    write_container(path, SHAPE, lambda l: synth.layer_params(SHAPE, l, seed=0), synth.head_params(SHAPE, seed=0))
+    say("tiny model from container")
+    dm2 = DeviceModel.load(path, max_batch=8, max_pos=4096)
+    prompt = synth.prompt_ids(PROMPT_LEN, SHAPE.vocab, seed=2)
+    a = _run(dm, [prompt], 8, layers=False)
+    b = _run(dm2, [prompt], 8, layers=False)
+    dm2.close()
+    np.testing.assert_array_equal(a["tokens"], b["tokens"])
+    np.testing.assert_array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32))

@@ -28,6 +28,9 @@ __all__ = [
     "nq_graph_launch", "nq_graph_kernel_count", "nq_graph_destroy", "nq_check_device_error",
     "nq_gemm_w4a16", "nq_attn_prefill", "NQPrefillIO", "nq_prefill_workspace_bytes", "nq_prefill",
     "nq_a8_bytes", "nq_quantize_a8", "nq_gemv_w4a8",
+    "NQTensorDesc", "NQ_TENSOR_PACKED", "NQ_TENSOR_F16", "nq_container_create", "nq_container_add",
+    "nq_container_finish", "nq_container_open", "nq_container_config", "nq_container_count",
+    "nq_container_tensor", "nq_container_tensor_at", "nq_container_verify", "nq_container_close",
     "header_symbols",
 ]
 
@@ -39,7 +42,8 @@ NQ_OK = 0
 NQ_MAT_PLAIN, NQ_MAT_QKV, NQ_MAT_GATE_UP, NQ_MAT_LM_HEAD = 0, 1, 2, 3
 NQ_EPI_STORE_F16, NQ_EPI_BIAS_F16, NQ_EPI_RESIDUAL_F16, NQ_EPI_SWIGLU_F16, NQ_EPI_STORE_F32 = 0, 1, 2, 3, 4
 STATUS_NAMES = {0: "NQ_OK", 1: "NQ_ERR_INVALID_ARG", 2: "NQ_ERR_UNSUPPORTED", 3: "NQ_ERR_OUT_OF_RANGE",
-                4: "NQ_ERR_HIP", 5: "NQ_ERR_STATE", 6: "NQ_ERR_DEVICE_FAULT"}
+                4: "NQ_ERR_HIP", 5: "NQ_ERR_STATE", 6: "NQ_ERR_DEVICE_FAULT", 7: "NQ_ERR_IO"}
+NQ_TENSOR_PACKED, NQ_TENSOR_F16 = 1, 2
 
 
 class NQError(RuntimeError):
@@ -72,6 +76,12 @@ class NQStepIO(ctypes.Structure):
                 ("tokens", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("logits", ctypes.c_void_p),
                 ("layer_out", ctypes.c_void_p), ("token_hist", ctypes.c_void_p), ("hist_len", ctypes.c_int32),
                 ("err_flag", ctypes.c_void_p)]
+
+
+class NQTensorDesc(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("role", ctypes.c_int32), ("mat_kind", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("bytes", ctypes.c_uint64)]
 
 
 class NQPrefillIO(ctypes.Structure):
@@ -126,6 +136,16 @@ _SIGS = {
     "nq_a8_bytes": (_S, [_I, _I]),
     "nq_quantize_a8": (_I, [_P, _I, _I, _P, _P]),
     "nq_gemv_w4a8": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P]),
+    "nq_container_create": (_I, [ctypes.c_char_p, _CFG, _I, ctypes.POINTER(_P)]),
+    "nq_container_add": (_I, [_P, ctypes.POINTER(NQTensorDesc), _P]),
+    "nq_container_finish": (_I, [_P]),
+    "nq_container_open": (_I, [ctypes.c_char_p, ctypes.POINTER(_P)]),
+    "nq_container_config": (_I, [_P, _CFG]),
+    "nq_container_count": (_I, [_P]),
+    "nq_container_tensor": (_I, [_P, ctypes.c_char_p, ctypes.POINTER(NQTensorDesc), ctypes.POINTER(_P)]),
+    "nq_container_tensor_at": (_I, [_P, _I, ctypes.POINTER(NQTensorDesc), ctypes.POINTER(_P)]),
+    "nq_container_verify": (_I, [_P]),
+    "nq_container_close": (None, [_P]),
 }
 
 _lib = None
@@ -366,3 +386,64 @@ def nq_prefill_workspace_bytes(cfg: NQConfig, chunk: int) -> int:
 
 def nq_prefill(m, kv, io: NQPrefillIO, stream=None) -> None:
     _check(lib().nq_prefill(m, kv, ctypes.byref(io), _stream(stream)), "nq_prefill")
+
+
+# ------------------------------------------------------------------ packed-weight container
+
+def nq_container_create(path: str, cfg: NQConfig, n_tensors: int):
+    h = _P()
+    _check(lib().nq_container_create(os.fsencode(path), ctypes.byref(cfg), n_tensors, ctypes.byref(h)),
+           "nq_container_create")
+    return h.value
+
+
+def nq_container_add(w, name: str, role: int, N: int, K: int, data: np.ndarray, mat_kind: int = 0,
+                     head_dim: int = 0) -> None:
+    data = np.ascontiguousarray(data)
+    d = NQTensorDesc(name.encode(), role, mat_kind, N, K, head_dim, data.nbytes)
+    _check(lib().nq_container_add(w, ctypes.byref(d), _ptr(data)), "nq_container_add")
+
+
+def nq_container_finish(w) -> None:
+    _check(lib().nq_container_finish(w), "nq_container_finish")
+
+
+def nq_container_open(path: str):
+    h = _P()
+    _check(lib().nq_container_open(os.fsencode(path), ctypes.byref(h)), "nq_container_open")
+    return h.value
+
+
+def nq_container_config(c) -> NQConfig:
+    cfg = NQConfig()
+    _check(lib().nq_container_config(c, ctypes.byref(cfg)), "nq_container_config")
+    return cfg
+
+
+def nq_container_count(c) -> int:
+    return lib().nq_container_count(c)
+
+
+def _tensor_view(d: NQTensorDesc, p: int) -> np.ndarray:
+    return np.ctypeslib.as_array(ctypes.cast(p, ctypes.POINTER(ctypes.c_uint8)), shape=(d.bytes,))
+
+
+def nq_container_tensor(c, name: str):
+    """(description, read-only uint8 view of the mapped bytes) of a tensor."""
+    d, p = NQTensorDesc(), _P()
+    _check(lib().nq_container_tensor(c, name.encode(), ctypes.byref(d), ctypes.byref(p)), "nq_container_tensor")
+    return d, _tensor_view(d, p.value)
+
+
+def nq_container_tensor_at(c, index: int):
+    d, p = NQTensorDesc(), _P()
+    _check(lib().nq_container_tensor_at(c, index, ctypes.byref(d), ctypes.byref(p)), "nq_container_tensor_at")
+    return d, _tensor_view(d, p.value)
+
+
+def nq_container_verify(c) -> None:
+    _check(lib().nq_container_verify(c), "nq_container_verify")
+
+
+def nq_container_close(c) -> None:
+    lib().nq_container_close(c)

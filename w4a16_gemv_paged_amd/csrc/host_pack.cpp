@@ -132,6 +132,7 @@ const char* nq_status_str(nq_status s) {
     case NQ_ERR_HIP: return "NQ_ERR_HIP";
     case NQ_ERR_STATE: return "NQ_ERR_STATE";
     case NQ_ERR_DEVICE_FAULT: return "NQ_ERR_DEVICE_FAULT";
+    case NQ_ERR_IO: return "NQ_ERR_IO";
   }
   return "NQ_ERR_UNKNOWN";
 }

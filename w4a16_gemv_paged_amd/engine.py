@@ -9,11 +9,14 @@ stream; every arithmetic step runs in libnq.
 from __future__ import annotations
 
 import ctypes
+import os
 
 import numpy as np
 import torch
 
 from . import (NQConfig, NQLayerPtrs, NQStepIO, NQ_MAT_PLAIN, NQ_MAT_QKV, NQ_MAT_GATE_UP, NQ_MAT_LM_HEAD,
+               NQ_TENSOR_PACKED, NQ_TENSOR_F16, nq_container_create, nq_container_add, nq_container_finish,
+               nq_container_open, nq_container_config, nq_container_tensor, nq_container_close,
                nq_pack_weights, nq_model_create, nq_model_bind_layer, nq_model_bind_head, nq_model_bind_rope,
                nq_rope_table_fill, nq_workspace_bytes, nq_model_bind_workspace, nq_model_destroy,
                nq_kv_pool_bytes, nq_kv_alloc, nq_kv_free, nq_decode_step, nq_graph_capture, nq_graph_launch,
@@ -26,8 +29,29 @@ def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
     return t.to(device, non_blocking=False)
 
 
-def _f16_dev(a, device):
-    return to_device(np.asarray(a, np.float16).view(np.int16), device)
+# Per-layer tensors of a model, in the order of nq_layer_ptrs, and the head's.
+LAYER_TENSORS = ("qkv", "qkv_bias", "o", "gate_up", "down", "attn_norm", "mlp_norm")
+HEAD_TENSORS = ("embed", "final_norm", "lm_head")
+
+
+def _pack_layer(p: dict, head_dim: int) -> dict:
+    """Host tensors of one layer: the four packed projections (uint8) and the
+    fp16 bias and norm gains."""
+    return {
+        "qkv": nq_pack_weights(np.concatenate([p["wq"], p["wk"], p["wv"]]), NQ_MAT_QKV, head_dim),
+        "qkv_bias": np.concatenate([p["bq"], p["bk"], p["bv"]]).astype(np.float16),
+        "o": nq_pack_weights(p["wo"], NQ_MAT_PLAIN),
+        "gate_up": nq_pack_weights(np.concatenate([p["wg"], p["wu"]]), NQ_MAT_GATE_UP),
+        "down": nq_pack_weights(p["wd"], NQ_MAT_PLAIN),
+        "attn_norm": np.asarray(p["g1"], np.float16),
+        "mlp_norm": np.asarray(p["g2"], np.float16),
+    }
+
+
+def _dev_bytes(a: np.ndarray, device) -> torch.Tensor:
+    """Upload host bytes (packed uint8, or fp16 kept as int16 bits)."""
+    a = np.ascontiguousarray(a)
+    return to_device(a.view(np.int16) if a.dtype == np.float16 else a, device)
 
 
 class DeviceModel:
@@ -35,43 +59,73 @@ class DeviceModel:
 
     ``layer_params(l)`` returns the parameter dict of layer l (float32
     wq/wk/wv/wo/wg/wu/wd, float16 bq/bk/bv/g1/g2); ``head`` holds float16
-    embed/g_final and float32 lm_head. Host copies are dropped after upload."""
+    embed/g_final and float32 lm_head. The weights are packed on the host and
+    uploaded layer by layer; host copies are dropped after upload.
+    ``DeviceModel.load`` builds the same model from a packed-weight container
+    instead, with no repacking."""
 
     def __init__(self, shape, layer_params, head: dict, max_batch: int, max_pos: int, device="cuda"):
+        self._setup(shape, max_batch, max_pos, device)
+        # draw and pack layer l+1 on a helper thread while layer l is uploaded
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(1) as ex:
+            nxt = ex.submit(lambda l: _pack_layer(layer_params(l), shape.head_dim), 0)
+            for li in range(shape.layers):
+                t = nxt.result()
+                if li + 1 < shape.layers:
+                    nxt = ex.submit(lambda l: _pack_layer(layer_params(l), shape.head_dim), li + 1)
+                self._bind_layer(li, [t[n] for n in LAYER_TENSORS])
+                del t
+        self._bind_head(head["embed"], head["g_final"], nq_pack_weights(head["lm_head"], NQ_MAT_LM_HEAD))
+
+    @classmethod
+    def load(cls, path: str, max_batch: int, max_pos: int, device="cuda") -> "DeviceModel":
+        """The model stored in a packed-weight container (``write_container``)."""
+        from types import SimpleNamespace
+        c = nq_container_open(path)
+        try:
+            cfg = nq_container_config(c)
+            shape = SimpleNamespace(name=os.path.basename(path), layers=cfg.layers, hidden=cfg.hidden,
+                                    intermediate=cfg.intermediate, n_heads=cfg.n_heads,
+                                    n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, vocab=cfg.vocab,
+                                    rms_eps=cfg.rms_eps, rope_theta=cfg.rope_theta)
+            self = cls.__new__(cls)
+            self._setup(shape, max_batch, max_pos, device)
+
+            def get(name):
+                d, view = nq_container_tensor(c, name)
+                return view.view(np.float16) if d.role == NQ_TENSOR_F16 else view
+
+            for li in range(cfg.layers):
+                self._bind_layer(li, [get(f"layer.{li}.{n}") for n in LAYER_TENSORS])
+            self._bind_head(*[get(n) for n in HEAD_TENSORS])
+        finally:
+            nq_container_close(c)   # the device copies are complete (synchronous uploads)
+        return self
+
+    def _setup(self, shape, max_batch, max_pos, device):
         self.shape = shape
         self.device = device
         self.cfg = NQConfig.from_shape(shape, max_batch, max_pos)
         self.handle = nq_model_create(self.cfg)
         self._keep = []
         self.layers = []
-        d = shape.head_dim
-        # draw layer l+1 on a helper thread while layer l is packed and uploaded
-        from concurrent.futures import ThreadPoolExecutor
-        with ThreadPoolExecutor(1) as ex:
-            nxt = ex.submit(layer_params, 0)
-            for li in range(shape.layers):
-                p = nxt.result()
-                if li + 1 < shape.layers:
-                    nxt = ex.submit(layer_params, li + 1)
-                qkv = nq_pack_weights(np.concatenate([p["wq"], p["wk"], p["wv"]]), NQ_MAT_QKV, d)
-                o = nq_pack_weights(p["wo"], NQ_MAT_PLAIN)
-                gu = nq_pack_weights(np.concatenate([p["wg"], p["wu"]]), NQ_MAT_GATE_UP)
-                dn = nq_pack_weights(p["wd"], NQ_MAT_PLAIN)
-                bias = np.concatenate([p["bq"], p["bk"], p["bv"]]).astype(np.float16)
-                names = ("qkv", "bias", "o", "gate_up", "down", "g1", "g2")
-                ts = [to_device(qkv, device), _f16_dev(bias, device), to_device(o, device), to_device(gu, device),
-                      to_device(dn, device), _f16_dev(p["g1"], device), _f16_dev(p["g2"], device)]
-                self._keep.extend(ts)
-                self.layers.append(dict(zip(names, ts)))
-                nq_model_bind_layer(self.handle, li, NQLayerPtrs(*[t.data_ptr() for t in ts]))
-                del p, qkv, o, gu, dn
-        self.embed = _f16_dev(head["embed"], device)
-        self.g_final = _f16_dev(head["g_final"], device)
-        self.lm = to_device(nq_pack_weights(head["lm_head"], NQ_MAT_LM_HEAD), device)
-        nq_model_bind_head(self.handle, self.embed, self.g_final, self.lm)
-        self.rope = to_device(nq_rope_table_fill(self.cfg), device)
-        nq_model_bind_rope(self.handle, self.rope)
         self.ws = None
+
+    def _bind_layer(self, li: int, host: list):
+        ts = [_dev_bytes(a, self.device) for a in host]
+        names = ("qkv", "bias", "o", "gate_up", "down", "g1", "g2")
+        self._keep.extend(ts)
+        self.layers.append(dict(zip(names, ts)))
+        nq_model_bind_layer(self.handle, li, NQLayerPtrs(*[t.data_ptr() for t in ts]))
+
+    def _bind_head(self, embed, g_final, lm_packed):
+        self.embed = _dev_bytes(np.asarray(embed, np.float16), self.device)
+        self.g_final = _dev_bytes(np.asarray(g_final, np.float16), self.device)
+        self.lm = _dev_bytes(lm_packed, self.device)
+        nq_model_bind_head(self.handle, self.embed, self.g_final, self.lm)
+        self.rope = to_device(nq_rope_table_fill(self.cfg), self.device)
+        nq_model_bind_rope(self.handle, self.rope)
 
     def weight_bytes(self) -> int:
         n = sum(t.numel() * t.element_size() for t in self._keep)
@@ -178,6 +232,38 @@ class Prefill:
 
     def check(self, stream=None):
         nq_check_device_error(self.err, stream)
+
+
+def write_container(path: str, shape, layer_params, head: dict) -> None:
+    """Packs a model (``layer_params(l)`` and ``head`` as for DeviceModel) into a
+    packed-weight container file, one layer at a time."""
+    cfg = NQConfig.from_shape(shape, 1, 1)
+    w = nq_container_create(path, cfg, len(LAYER_TENSORS) * shape.layers + len(HEAD_TENSORS))
+    try:
+        for li in range(shape.layers):
+            t = _pack_layer(layer_params(li), shape.head_dim)
+            H, I, d = shape.hidden, shape.intermediate, shape.head_dim
+            qkv_n = (shape.n_heads + 2 * shape.n_kv_heads) * d
+            packed = {"qkv": (qkv_n, H, NQ_MAT_QKV, d), "o": (H, shape.n_heads * d, NQ_MAT_PLAIN, 0),
+                      "gate_up": (2 * I, H, NQ_MAT_GATE_UP, 0), "down": (H, I, NQ_MAT_PLAIN, 0)}
+            for name in LAYER_TENSORS:
+                a = t[name]
+                if name in packed:
+                    N, K, kind, hd = packed[name]
+                    nq_container_add(w, f"layer.{li}.{name}", NQ_TENSOR_PACKED, N, K, a, kind, hd)
+                else:
+                    nq_container_add(w, f"layer.{li}.{name}", NQ_TENSOR_F16, a.size, 1, a)
+        nq_container_add(w, "embed", NQ_TENSOR_F16, shape.vocab, shape.hidden, np.asarray(head["embed"], np.float16))
+        nq_container_add(w, "final_norm", NQ_TENSOR_F16, shape.hidden, 1, np.asarray(head["g_final"], np.float16))
+        nq_container_add(w, "lm_head", NQ_TENSOR_PACKED, shape.vocab, shape.hidden,
+                         nq_pack_weights(head["lm_head"], NQ_MAT_LM_HEAD), NQ_MAT_LM_HEAD)
+    except BaseException:
+        try:
+            nq_container_finish(w)   # frees the writer; the count check fails, which is expected here
+        except Exception:
+            pass
+        raise
+    nq_container_finish(w)
 
 
 def run_greedy(st: Stepper, prompts, n_gen: int, use_graph: bool = False, stream=None,

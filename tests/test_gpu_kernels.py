@@ -267,6 +267,38 @@ def test_attention_independent_of_page_placement():
     nq.nq_kv_free(hb)
 
 
+def test_attention_split_merge_reuses_workspace():
+    """Split partials merged with the log-sum-exp rule: three calls on one
+    workspace give bit-identical outputs. The workspace starts as NaN bit
+    patterns: an empty split's output rows (a zero length, and the pages past
+    each short sequence) are never written and must never be used."""
+    lens = [3, 700, 0, 2000]
+    inp, cfg, pool, h, pool_np = _attn_setup(ATT7B, lens, seed=8)
+    batch, max_pages = len(lens), inp["page_table"].shape[1]
+    wsb = nq.nq_attn_workspace_bytes(cfg, batch, max_pages)
+    ws = torch.full((wsb,), 0xFF, dtype=torch.uint8, device="cuda")
+    live = [b for b, L in enumerate(lens) if L > 0]
+    ref = dict(zip(live, oracle.paged_attention(inp["q"][live], pool_np[0], inp["page_table"][live],
+                                                inp["lens"][live])))
+    outs = []
+    for call in range(3):
+        say("attention split reuse", call)
+        out = torch.empty(batch, cfg.n_heads, cfg.head_dim, dtype=torch.float16, device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        nq.nq_attn_decode(h, 0, batch, dev(inp["q"]), dev(inp["page_table"]), max_pages, dev(inp["lens"]), out,
+                          ws, wsb, err)
+        nq.nq_check_device_error(err)
+        outs.append(host(out))
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(outs[0][b] == 0)
+        else:
+            assert rel_inf(outs[0][b], ref[b]) < TOL_LAYER, (b, L)
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o.view(np.uint16), outs[0].view(np.uint16))
+    nq.nq_kv_free(h)
+
+
 @pytest.mark.parametrize("lens", [[511, 4097, 32767]])
 def test_attention_full_context_lengths(lens):
     """The attention sweep lengths of the 7B shape (tails of 15, 1 and 15 tokens)."""

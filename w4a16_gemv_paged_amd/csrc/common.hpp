@@ -109,7 +109,7 @@ struct AttnPlan {
 AttnPlan attn_plan(int32_t batch, int32_t n_kv, int32_t max_pages);
 // Largest page-table width the attention kernels cover (64 splits x 8 waves x
 // 64 pages per wave = 32768 pages, 524288 tokens).
-constexpr int32_t kAttnMaxPages = 64 * 8 * 64;
+constexpr int32_t kAttnMaxPages = 64 * 4 * 128;  // splits x waves x pages per wave
 size_t attn_partial_bytes(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t splits);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

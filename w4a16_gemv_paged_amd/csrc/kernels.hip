@@ -939,11 +939,17 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
 // Scratch", FAQ on the barrier inside a warp-id branch). When one workgroup
 // covers the whole context it writes the output; otherwise workgroups write
 // (max, sum, output) partials and the combine kernel merges them with the
-// log-sum-exp rule.
+// log-sum-exp rule. Workgroups are 4 waves, so that three of them fit on a CU
+// at the kernel's register count: 12 waves per CU where one 8-wave workgroup
+// gives 8, and a finer grain for ragged batches.
 
-constexpr int kAttnWaves = 8;
+constexpr int kAttnWaves = 4;
 constexpr int kMaxSplits = 64;
-constexpr int kMaxPagesPerWave = 64;  // page ids held one per lane
+constexpr int kMaxPagesPerWave = kAttnMaxPages / (kMaxSplits * kAttnWaves);
+constexpr int kPidRegs = (kMaxPagesPerWave + 63) / 64;  // page ids held one per lane and register
+// waves per SIMD the register budget is sized for (at most 168 registers):
+// whole workgroups of kAttnWaves waves on the 4 SIMDs of a CU
+constexpr int kAttnWavesPerSimd = kAttnWaves == 4 ? 3 : 2;
 static_assert(kAttnMaxPages == kMaxSplits * kAttnWaves * kMaxPagesPerWave, "attention page limit");
 constexpr int kAttnTargetGroups = 512;
 
@@ -982,7 +988,8 @@ struct AttnParams {
 };
 
 template <int D, int REP>
-__global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnParams a) {
+__global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(kAttnWavesPerSimd)))
+void attn_decode_kernel(AttnParams a) {
   static_assert((D == 64 || D == 128) && REP >= 1 && REP <= 16, "unsupported head shape");
   constexpr int NW = kAttnWaves;
   constexpr int KJ = D / 32;  // score MFMAs per page
@@ -1008,11 +1015,19 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnParams
   }
   // this wave's page ids, one per lane; they do not depend on the length, so
   // these loads overlap with the length load
-  int pid = -1;
-  {
-    const int myp = p0 + w + lane * NW;
-    if (lane < kMaxPagesPerWave && myp < pend) pid = a.pt[static_cast<int64_t>(b) * a.max_pages + myp];
+  int pid[kPidRegs];
+#pragma unroll
+  for (int r = 0; r < kPidRegs; ++r) {
+    const int myp = p0 + w + (lane + 64 * r) * NW;
+    pid[r] = myp < pend ? a.pt[static_cast<int64_t>(b) * a.max_pages + myp] : -1;
   }
+  auto page_id = [&](int k) {  // k is wave-uniform
+    int id = __builtin_amdgcn_readlane(pid[0], k & 63);
+#pragma unroll
+    for (int r = 1; r < kPidRegs; ++r)
+      if ((k >> 6) == r) id = __builtin_amdgcn_readlane(pid[r], k & 63);
+    return id;
+  };
   const int len = __builtin_amdgcn_readfirstlane(a.lens[b] + a.len_add);
   const int npages = min((len + kPageTokens - 1) / kPageTokens, a.max_pages);
   if (s == 0 && tid == 0 && len > a.max_pages * kPageTokens) raise_flag(a.err, 2);
@@ -1046,7 +1061,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnParams
   // page k of this wave: K rows t = r16 (dims 32j + 8*g4 ..), V^T rows d = 16c + r16
   // (tokens 4*g4 .. +3). An id outside the pool reads page 0 and is skipped.
   auto load = [&](int k, half8 (&kf)[KJ], half4 (&vf)[VC]) {
-    const int id = __builtin_amdgcn_readlane(pid, k);
+    const int id = page_id(k);
     const int idc = (id >= 0 && id < a.num_pages) ? id : 0;
     const int64_t base = (static_cast<int64_t>(idc) * a.n_kv + kvh) * (kPageTokens * D);
     const half_t* kb = a.kp + base + r16 * D + 8 * g4;
@@ -1060,7 +1075,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnParams
   // the loop), so the loop body stays free of branches around memory ops.
   bool bad = false;
   auto compute = [&](int k, const half8 (&kf)[KJ], half4 (&vf)[VC]) {
-    const int id = __builtin_amdgcn_readlane(pid, k);
+    const int id = page_id(k);
     const bool okp = id >= 0 && id < a.num_pages;
     bad |= !okp;
     const int valid = okp ? min(kPageTokens, len - (p0 + w + k * NW) * kPageTokens) : 0;
@@ -1161,6 +1176,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams a) {
   constexpr int kEarly = 8;  // partials per thread loaded before the weights are known
   __shared__ float wgt[kMaxSplits];
   __shared__ float inv_l;
+  __shared__ int n_live;
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int S = a.S;
   const int64_t rb = (static_cast<int64_t>(b) * a.n_heads + h) * S;
@@ -1176,7 +1192,13 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams a) {
     float L = f * l0;
     for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
     if (d < S) wgt[d] = f;
-    if (d == 0) inv_l = L > 0.0f ? 1.0f / L : 0.0f;
+    // splits past the last one with a weight hold nothing (the pages of a
+    // sequence are a prefix of its table row)
+    const unsigned long long live = __ballot(f != 0.0f);
+    if (d == 0) {
+      inv_l = L > 0.0f ? 1.0f / L : 0.0f;
+      n_live = live ? 64 - __clzll(static_cast<long long>(live)) : 0;
+    }
   }
   __syncthreads();
   // an empty split's output row was never written: its weight selects 0, not 0 * (stale value)
@@ -1184,8 +1206,14 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams a) {
 #pragma unroll
   for (int s = 0; s < kEarly; ++s)
     if (s < S && wgt[s] != 0.0f) O = fmaf(wgt[s], pv[s], O);
-  for (int s = kEarly; s < S; ++s)
-    if (wgt[s] != 0.0f) O = fmaf(wgt[s], a.po[(rb + s) * D + d], O);
+  for (int s0 = kEarly; s0 < n_live; s0 += kEarly) {  // later splits kEarly at a time, loads issued together
+#pragma unroll
+    for (int s = 0; s < kEarly; ++s)
+      pv[s] = (s0 + s < S && wgt[s0 + s] != 0.0f) ? a.po[(rb + s0 + s) * D + d] : 0.0f;
+#pragma unroll
+    for (int s = 0; s < kEarly; ++s)
+      if (s0 + s < S && wgt[s0 + s] != 0.0f) O = fmaf(wgt[s0 + s], pv[s], O);
+  }
   a.out[(static_cast<int64_t>(b) * a.n_heads + h) * D + d] = static_cast<half_t>(O * inv_l);
 }
 

@@ -358,6 +358,12 @@ size_t nq_attn_workspace_bytes(const nq_config* cfg, int32_t batch, int32_t max_
  * q: device fp16 [batch][n_heads][head_dim]; out: device fp16, same shape.
  * lens: device int32 [batch] (0 gives a zero output row).
  * max_pages: page_table row stride, 1..32768 (NQ_ERR_OUT_OF_RANGE beyond).
+ * batch: 1..64 when the pages are split by length (batch > 1 and max_pages > 4);
+ * with batch * max_pages beyond what 1024 workgroups per KV head of at most 512
+ * pages cover, the call fails with NQ_ERR_OUT_OF_RANGE (and the workspace
+ * size is 0). The pages of a sequence are spread over the splits by the
+ * current lengths, so results agree with a batch-1 call within rounding, not
+ * bitwise.
  * workspace: device, nq_attn_workspace_bytes(cfg, batch, max_pages) bytes for
  * the split partials; calls that share a workspace must not overlap.
  * err_flag: optional device int32 (bad page id or length -> ORs 2, output 0).

@@ -323,6 +323,42 @@ def test_attention_batch8_ragged_full_range():
     nq.nq_kv_free(h)
 
 
+@pytest.mark.parametrize("batch,hi,seed", [(3, 3000, 21), (16, 1200, 22), (64, 300, 23)])
+def test_attention_split_by_length_large_batch(batch, hi, seed):
+    """Batches above one split every sequence's pages by the current lengths
+    over a fixed grid: ragged lengths (zeros included) up to 64 sequences,
+    against the oracle; a zero length gives a zero row."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, hi, size=batch)
+    lens[0], lens[-1] = 0, hi                      # an empty sequence and the longest one
+    shape = ATTTINY if batch > 8 else ATT7B
+    say("attention by length", batch, int(lens.sum()))
+    inp, cfg, pool, h, pool_np = _attn_setup(shape, lens.tolist(), seed=seed)
+    got = _attn_run(cfg, h, inp, batch)
+    live = [b for b in range(batch) if lens[b] > 0]
+    ref = oracle.paged_attention(inp["q"][live], pool_np[0], inp["page_table"][live], inp["lens"][live])
+    for i, b in enumerate(live):
+        assert rel_inf(got[b], ref[i]) < TOL_LAYER, (b, lens[b])
+    assert np.all(got[0] == 0)
+    nq.nq_kv_free(h)
+
+
+def test_attention_rejects_batch_beyond_split_grid():
+    """64 sequences of 32768-page tables need more than 1024 workgroups of 512
+    pages per KV head: refused before any launch, and the workspace size is 0."""
+    cfg, pool, h = _kv_handle(ATTTINY, 8)
+    assert nq.nq_attn_workspace_bytes(cfg, 64, 32768) == 0
+    q = torch.zeros(64, cfg.n_heads, cfg.head_dim, dtype=torch.float16, device="cuda")
+    pt = torch.zeros(64, 32768, dtype=torch.int32, device="cuda")
+    lens = torch.ones(64, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    say("attention oversized batch refused")
+    with pytest.raises(nq.NQError) as e:
+        nq.nq_attn_decode(h, 0, 64, q, pt, 32768, lens, torch.empty_like(q), ws, ws.numel(), None)
+    assert e.value.status == 3  # NQ_ERR_OUT_OF_RANGE
+    nq.nq_kv_free(h)
+
+
 def test_attention_bad_page_id_sets_flag():
     lens = [40]
     inp, cfg, pool, h, _ = _attn_setup(ATTTINY, lens)

@@ -194,6 +194,10 @@ def test_config_check_and_sizes():
     assert nq.nq_workspace_bytes(cfg, 1, 48) > 0
     assert nq.nq_workspace_bytes(cfg, 9, 48) == 0
     assert nq.nq_attn_workspace_bytes(cfg, 8, 2048) > 0
+    # every decode-step batch covers the widest table; 64 sequences of it do not
+    assert nq.nq_workspace_bytes(cfg, 8, 32768) > 0
+    assert nq.nq_attn_workspace_bytes(cfg, 64, 4096) > 0
+    assert nq.nq_attn_workspace_bytes(cfg, 64, 32768) == 0
 
 
 def test_rope_table_matches_definition():

@@ -100,16 +100,22 @@ struct AttnArgs {
   float* part_ml = nullptr;         // [B][nh][S][2]
   int32_t batch = 1, n_heads = 0, n_kv = 0, head_dim = 0;
   int32_t splits = 1, per = 8;      // from attn_plan(batch, n_kv, max_pages)
+  int32_t dyn = 0;                  // the same plan's split mode
   int32_t* err = nullptr;
 };
-// Split of a sequence's pages over workgroups: S splits of ``per`` pages each.
+// Split of the pages over workgroups. Fixed (dyn 0): S splits of ``per`` pages
+// of every sequence. By length (dyn 1): S workgroups per KV head share all
+// sequences' pages, ``per`` the most pages one split can get. S = 0: the batch
+// and table width are beyond what the kernels cover.
 struct AttnPlan {
-  int32_t S = 1, per = 8;
+  int32_t S = 1, per = 8, dyn = 0;
 };
+constexpr int32_t kAttnMaxSplits = 1024;  // workgroups per KV head
+constexpr int32_t kAttnMaxBatch = 64;     // sequences of a split-by-length launch
 AttnPlan attn_plan(int32_t batch, int32_t n_kv, int32_t max_pages);
-// Largest page-table width the attention kernels cover (64 splits x 8 waves x
-// 64 pages per wave = 32768 pages, 524288 tokens).
-constexpr int32_t kAttnMaxPages = 64 * 4 * 128;  // splits x waves x pages per wave
+// Largest page-table width the attention kernels cover (32768 pages, 524288
+// tokens); the batch times the width is bounded further by attn_plan (S = 0).
+constexpr int32_t kAttnMaxPages = 32768;
 size_t attn_partial_bytes(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t splits);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

@@ -231,14 +231,14 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
     auto load_scales = [&](int w0) {
       const int bi = w0 + col;
       const int g = c0 + ksi + p.ks * bi;
-      return __builtin_amdgcn_raw_buffer_load_b64(srs, (col < kDepth && bi < n_c) ? g * 32 + kb * 8 : sbytes, 0, 0);
+      return __builtin_amdgcn_raw_buffer_load_b64(srs, (col < kDepth && bi < n_c) ? g * 32 + kb * 8 : sbytes, 0, kStreamOnce);
     };
     u32x2 swin = load_scales(0);
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
       const bool ok = u < n_c;
       const int g = c0 + ksi + p.ks * u;
-      wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff, ok ? g * kBlockBytes : wbytes, 0);
+      wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff, ok ? g * kBlockBytes : wbytes, kStreamOnce);
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kDepth + 1));  // this wave's LDS writes have landed
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
           sprev = row_bcast2(swin, u);
           if (i + kDepth < n_c) {  // refill the slot just consumed
             const int gn = c0 + ksi + p.ks * (i + kDepth);
-            wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff, gn * kBlockBytes, 0);
+            wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff, gn * kBlockBytes, kStreamOnce);
           }
         }
       }
@@ -571,11 +571,11 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvPara
     chunk_range(q, g0, g1, j);
     const bool in = q < Q;
     const int fs = (in && col < CH && g0 + col < g1) ? j * G + g0 + col : nb;
-    sc = __builtin_amdgcn_raw_buffer_load_b64(srs, fs * 32 + kb * 8, 0, 0);
+    sc = __builtin_amdgcn_raw_buffer_load_b64(srs, fs * 32 + kb * 8, 0, kStreamOnce);
 #pragma unroll
     for (int s2 = 0; s2 < CH; ++s2) {
       const int f = (in && g0 + s2 < g1) ? j * G + g0 + s2 : nb;   // nb: out of range, reads 0
-      w[s2] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff, f * kBlockBytes, 0);
+      w[s2] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff, f * kBlockBytes, kStreamOnce);
     }
   };
   auto compute_chunk = [&](int q, const u32x4 (&w)[CH], const u32x2& sc) {
@@ -939,32 +939,70 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
 // Scratch", FAQ on the barrier inside a warp-id branch). When one workgroup
 // covers the whole context it writes the output; otherwise workgroups write
 // (max, sum, output) partials and the combine kernel merges them with the
-// log-sum-exp rule. Workgroups are 4 waves, so that three of them fit on a CU
+// log-sum-exp rule. The split follows the actual lengths, not the table
+// width: every workgroup of a fixed grid of S per KV head reads the lengths,
+// takes per = the page count per split that spreads all sequences' pages over
+// the grid, and finds its (sequence, split) from the running sum of the
+// sequences' split counts ceil(pages_b / per). A ragged batch then gives every
+// workgroup about the same number of pages, and the grid (hence a captured
+// graph) does not depend on the lengths. Workgroups are 4 waves, so that three of them fit on a CU
 // at the kernel's register count: 12 waves per CU where one 8-wave workgroup
 // gives 8, and a finer grain for ragged batches.
 
 constexpr int kAttnWaves = 4;
-constexpr int kMaxSplits = 64;
-constexpr int kMaxPagesPerWave = kAttnMaxPages / (kMaxSplits * kAttnWaves);
+constexpr int kMaxPagesPerWave = 128;  // a split holds at most kAttnWaves * 128 pages
 constexpr int kPidRegs = (kMaxPagesPerWave + 63) / 64;  // page ids held one per lane and register
 // waves per SIMD the register budget is sized for (at most 168 registers):
 // whole workgroups of kAttnWaves waves on the 4 SIMDs of a CU
 constexpr int kAttnWavesPerSimd = kAttnWaves == 4 ? 3 : 2;
-static_assert(kAttnMaxPages == kMaxSplits * kAttnWaves * kMaxPagesPerWave, "attention page limit");
-constexpr int kAttnTargetGroups = 512;
+static_assert(kAttnMaxSplits % 64 == 0, "combine weight slots");
+constexpr int kAttnTargetGroups = 768;  // three 4-wave workgroups per CU
+
+// Pages per split for S workgroups per KV head over B sequences holding P
+// pages in all: a multiple of the wave count such that sum_b ceil(pages_b /
+// per) <= S (each ceil adds less than one split, hence S - B).
+__host__ __device__ __forceinline__ int attn_pages_per_split(int P, int S, int B) {
+  const int room = S - B > 0 ? S - B : 1;
+  int per = (P + room - 1) / room;
+  per = (per + kAttnWaves - 1) / kAttnWaves * kAttnWaves;
+  return per > kAttnWaves ? per : kAttnWaves;
+}
 
 AttnPlan attn_plan(int32_t batch, int32_t n_kv, int32_t max_pages) {
   AttnPlan p;
-  const int groups = std::max(1, batch * n_kv);
-  int S = std::max(1, (kAttnTargetGroups + groups - 1) / groups);
-  S = std::min(S, std::max(1, (max_pages + kAttnWaves - 1) / kAttnWaves));  // >= one page per wave
-  S = std::min(S, kMaxSplits);
-  int per = (max_pages + S - 1) / S;
-  per = std::max(per, (max_pages + kMaxSplits - 1) / kMaxSplits);
-  per = (per + kAttnWaves - 1) / kAttnWaves * kAttnWaves;
-  per = std::min(std::max(per, kAttnWaves), kAttnWaves * kMaxPagesPerWave);
-  p.per = per;
-  p.S = std::max(1, (max_pages + per - 1) / per);
+  if (batch < 1 || max_pages < 1) {
+    p.S = 0;
+    return p;
+  }
+  const int pages4 = (max_pages + kAttnWaves - 1) / kAttnWaves;
+  const int target = std::max(1, kAttnTargetGroups / std::max(1, n_kv));
+  if (max_pages <= kAttnWaves || (batch == 1 && pages4 <= target)) {
+    // fixed splits of one page per wave (one split when the table is that
+    // short): the page ids do not wait for the length, and a batch of one
+    // cannot be imbalanced
+    p.S = pages4;
+    p.per = kAttnWaves;
+    return p;
+  }
+  if (batch > kAttnMaxBatch) {
+    p.S = 0;
+    return p;
+  }
+  // splits by length: enough to fill the chip, no more than the table can use
+  // (one page per wave), at least one more than the batch, and enough that no
+  // wave holds more than kMaxPagesPerWave pages
+  const int64_t cap = static_cast<int64_t>(kAttnWaves) * kMaxPagesPerWave;
+  const int64_t all = static_cast<int64_t>(batch) * max_pages;
+  int64_t S = std::min<int64_t>(target, static_cast<int64_t>(batch) * pages4);
+  S = std::max<int64_t>(S, (all + cap - 1) / cap + batch);
+  S = std::max<int64_t>(S, batch + 1);
+  if (S > kAttnMaxSplits || attn_pages_per_split(static_cast<int>(all), static_cast<int>(S), batch) > cap) {
+    p.S = 0;  // beyond what the kernels cover
+    return p;
+  }
+  p.S = static_cast<int32_t>(S);
+  p.per = attn_pages_per_split(static_cast<int>(all), p.S, batch);  // the largest any lengths give
+  p.dyn = 1;
   return p;
 }
 
@@ -983,9 +1021,37 @@ struct AttnParams {
   half_t* out;
   float* po;
   float* pml;
-  int n_heads, n_kv, S, per;
+  int n_heads, n_kv, S, per, batch, dyn;
   int32_t* err;
 };
+
+// The split of workgroup w (of a.S per KV head) for the current lengths: lane
+// j < batch takes sequence j's page count; returns false for a workgroup past
+// the last split. Every lane gets the same (b, s, per, np_b).
+__device__ __forceinline__ bool attn_split_of(const AttnParams& a, int w, int& b, int& s, int& per, int& npb) {
+  const int lane = threadIdx.x & 63;
+  int np = 0;
+  if (lane < a.batch) {
+    const int L = a.lens[lane] + a.len_add;
+    np = L > 0 ? min((L + kPageTokens - 1) / kPageTokens, a.max_pages) : 0;
+  }
+  int P = np;
+  for (int o = 32; o >= 1; o >>= 1) P += __shfl_xor(P, o);
+  per = attn_pages_per_split(P, a.S, a.batch);
+  const int sb = (np + per - 1) / per;
+  int start = sb;  // inclusive running sum over lanes, then exclusive
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(start, o);
+    if (lane >= o) start += v;
+  }
+  start -= sb;
+  const unsigned long long hit = __ballot(sb > 0 && w >= start && w < start + sb);
+  if (!hit) return false;
+  b = __builtin_ctzll(hit);
+  s = w - __shfl(start, b);
+  npb = __shfl(np, b);
+  return true;
+}
 
 template <int D, int REP>
 __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(kAttnWavesPerSimd)))
@@ -998,12 +1064,19 @@ void attn_decode_kernel(AttnParams a) {
   __shared__ float red_m[NW][16], red_l[NW][16];
   __shared__ __align__(16) float red_o[NW][REP][DP];
 
-  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int kvh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int p0 = s * a.per;
-  const int pend = min(a.max_pages, p0 + a.per);
+  int b = blockIdx.z, s = blockIdx.x, per = a.per, npb = 0;
+  if (a.dyn) {  // split by the current lengths (block-uniform)
+    if (!attn_split_of(a, blockIdx.x, b, s, per, npb)) return;
+    b = __builtin_amdgcn_readfirstlane(b);
+    s = __builtin_amdgcn_readfirstlane(s);
+    per = __builtin_amdgcn_readfirstlane(per);
+  }
+  const int p0 = s * per;
+  const int pend = min(a.max_pages, p0 + per);
   // Q^T fragments: lane holds head r16, dims 32j + 8*g4 .. +7 (zero for the
   // padding heads r16 >= REP, which load head 0 and discard it)
   half8 qf[KJ];
@@ -1030,7 +1103,7 @@ void attn_decode_kernel(AttnParams a) {
   };
   const int len = __builtin_amdgcn_readfirstlane(a.lens[b] + a.len_add);
   const int npages = min((len + kPageTokens - 1) / kPageTokens, a.max_pages);
-  if (s == 0 && tid == 0 && len > a.max_pages * kPageTokens) raise_flag(a.err, 2);
+  if (s == 0 && tid == 0 && len > a.max_pages * kPageTokens) raise_flag(a.err, 2);  // (a length past the table)
   const int64_t row0 = (static_cast<int64_t>(b) * a.n_heads + kvh * REP) * a.S;
   if (len <= 0 || p0 >= npages) {  // block-uniform
     if (a.S == 1) {                // empty context: zero output
@@ -1168,53 +1241,105 @@ void attn_decode_kernel(AttnParams a) {
   }
 }
 
-// grid (n_heads, B), D threads: merge the S split partials of one query head
-// (maxima in log2 units). Every split wrote its row (an empty one with max
-// -inf), so nothing here waits for the length: the partial loads go out at once.
+// grid (n_heads, B), 1024 threads: merge the split partials of one query head
+// (maxima in log2 units). Thread group g of 1024 / D takes splits g, g + G,
+// ..., so a long split list is read G rows at a time; the group sums are then
+// added in group order (the result does not depend on timing). The splits of
+// sequence b are the ceil(pages_b / per) ones the attention kernel derived
+// from the same lengths; the first loads go out before that count is known.
 template <int D>
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams a) {
+__global__ __launch_bounds__(1024) void attn_combine_kernel(AttnParams a) {
+  constexpr int G = 1024 / D;
   constexpr int kEarly = 8;  // partials per thread loaded before the weights are known
-  __shared__ float wgt[kMaxSplits];
+  constexpr int kSlots = kAttnMaxSplits / 64;  // splits per lane in the weight pass
+  __shared__ float wgt[kAttnMaxSplits];
+  __shared__ float part[G][D];
   __shared__ float inv_l;
   __shared__ int n_live;
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int d = threadIdx.x % D, g = threadIdx.x / D;
   const int S = a.S;
   const int64_t rb = (static_cast<int64_t>(b) * a.n_heads + h) * S;
   float pv[kEarly];
 #pragma unroll
-  for (int s = 0; s < kEarly; ++s) pv[s] = s < S ? a.po[(rb + s) * D + d] : 0.0f;
-  if (d < 64) {  // one wave: max and softmax weights of the splits
-    const float m0 = d < S ? a.pml[(rb + d) * 2] : -INFINITY;
-    const float l0 = d < S ? a.pml[(rb + d) * 2 + 1] : 0.0f;
-    float M = m0;
+  for (int i = 0; i < kEarly; ++i) {
+    const int s = g + G * i;
+    pv[i] = s < S ? a.po[(rb + s) * D + d] : 0.0f;
+  }
+  if (threadIdx.x < 64) {  // one wave: the softmax weights of the splits
+    const int lane = threadIdx.x;
+    // fixed splits: every one wrote its row (an empty one with max -inf), so
+    // nothing waits for the length; splits by length: sequence b has the
+    // ceil(pages_b / per) the attention kernel derived from the same lengths
+    int sb = S;
+    if (a.dyn) {
+      int np = 0;
+      if (lane < a.batch) {
+        const int L = a.lens[lane] + a.len_add;
+        np = L > 0 ? min((L + kPageTokens - 1) / kPageTokens, a.max_pages) : 0;
+      }
+      int P = np;
+      for (int o = 32; o >= 1; o >>= 1) P += __shfl_xor(P, o);
+      const int per = attn_pages_per_split(P, S, a.batch);
+      sb = (__shfl(np, b) + per - 1) / per;
+    }
+    float m0[kSlots], l0[kSlots];
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) {
+      const int sj = lane + 64 * j;
+      m0[j] = sj < sb ? a.pml[(rb + sj) * 2] : -INFINITY;
+      l0[j] = sj < sb ? a.pml[(rb + sj) * 2 + 1] : 0.0f;
+      M = fmaxf(M, m0[j]);
+    }
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const float f = (m0 == -INFINITY) ? 0.0f : exp2f(m0 - M);
-    float L = f * l0;
-    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-    if (d < S) wgt[d] = f;
-    // splits past the last one with a weight hold nothing (the pages of a
-    // sequence are a prefix of its table row)
-    const unsigned long long live = __ballot(f != 0.0f);
-    if (d == 0) {
+    float L = 0.0f;
+    int last = -1;  // the last split with a weight: the ones after it hold nothing
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) {
+      const float f = (m0[j] == -INFINITY) ? 0.0f : exp2f(m0[j] - M);
+      L = fmaf(f, l0[j], L);
+      wgt[lane + 64 * j] = f;
+      if (f != 0.0f) last = lane + 64 * j;
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+      L += __shfl_xor(L, o);
+      last = max(last, __shfl_xor(last, o));
+    }
+    if (lane == 0) {
       inv_l = L > 0.0f ? 1.0f / L : 0.0f;
-      n_live = live ? 64 - __clzll(static_cast<long long>(live)) : 0;
+      n_live = last + 1;
     }
   }
   __syncthreads();
   // an empty split's output row was never written: its weight selects 0, not 0 * (stale value)
+  const int nl = n_live;
   float O = 0.0f;
 #pragma unroll
-  for (int s = 0; s < kEarly; ++s)
-    if (s < S && wgt[s] != 0.0f) O = fmaf(wgt[s], pv[s], O);
-  for (int s0 = kEarly; s0 < n_live; s0 += kEarly) {  // later splits kEarly at a time, loads issued together
-#pragma unroll
-    for (int s = 0; s < kEarly; ++s)
-      pv[s] = (s0 + s < S && wgt[s0 + s] != 0.0f) ? a.po[(rb + s0 + s) * D + d] : 0.0f;
-#pragma unroll
-    for (int s = 0; s < kEarly; ++s)
-      if (s0 + s < S && wgt[s0 + s] != 0.0f) O = fmaf(wgt[s0 + s], pv[s], O);
+  for (int i = 0; i < kEarly; ++i) {
+    const int s = g + G * i;
+    if (s < nl && wgt[s] != 0.0f) O = fmaf(wgt[s], pv[i], O);
   }
-  a.out[(static_cast<int64_t>(b) * a.n_heads + h) * D + d] = static_cast<half_t>(O * inv_l);
+  for (int s0 = G * kEarly; s0 < nl; s0 += G * kEarly) {  // later splits kEarly per thread at a time
+#pragma unroll
+    for (int i = 0; i < kEarly; ++i) {
+      const int s = s0 + g + G * i;
+      pv[i] = (s < nl && wgt[s] != 0.0f) ? a.po[(rb + s) * D + d] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kEarly; ++i) {
+      const int s = s0 + g + G * i;
+      if (s < nl && wgt[s] != 0.0f) O = fmaf(wgt[s], pv[i], O);
+    }
+  }
+  part[g][d] = O;
+  __syncthreads();
+  if (g == 0) {
+    float t = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) t += part[gg][d];
+    a.out[(static_cast<int64_t>(b) * a.n_heads + h) * D + d] = static_cast<half_t>(t * inv_l);
+  }
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
@@ -1234,13 +1359,18 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   p.n_kv = a.n_kv;
   p.S = a.splits;
   p.per = a.per;
+  p.batch = a.batch;
+  p.dyn = a.dyn;
   p.err = a.err;
   const int rep = a.n_heads / a.n_kv;
-  const dim3 grid(p.S, p.n_kv, a.batch), block(64 * kAttnWaves);
+  if (p.S < 1 || p.S > kAttnMaxSplits || (p.dyn && a.batch > kAttnMaxBatch)) return hipErrorInvalidValue;
+  // splits by length: S workgroups per KV head, each finds its (sequence,
+  // split); fixed splits: S per (KV head, sequence)
+  const dim3 grid(p.S, p.n_kv, p.dyn ? 1 : a.batch), block(64 * kAttnWaves);
 #define NQ_ATT(DD, RR)                                                                   \
   if (a.head_dim == DD && rep == RR) {                                                   \
     attn_decode_kernel<DD, RR><<<grid, block, 0, s>>>(p);                                \
-    if (p.S > 1) attn_combine_kernel<DD><<<dim3(a.n_heads, a.batch), dim3(DD), 0, s>>>(p); \
+    if (p.S > 1) attn_combine_kernel<DD><<<dim3(a.n_heads, a.batch), dim3(1024), 0, s>>>(p); \
     return hipGetLastError();                                                            \
   }
   NQ_ATT(128, 7) NQ_ATT(128, 8) NQ_ATT(128, 4) NQ_ATT(128, 2) NQ_ATT(128, 1)

@@ -182,6 +182,7 @@ int enqueue_step(nq_model* m, nq_kv* kv, const nq_step_io* io, hipStream_t s) {
     at.head_dim = c.head_dim;
     at.splits = w.attn.S;
     at.per = w.attn.per;
+    at.dyn = w.attn.dyn;
     at.err = err;
     if ((e = launch_attention(at, s)) != hipSuccess) return hip_fail(e, "attention launch"), -1;
 
@@ -580,6 +581,7 @@ nq_status nq_kv_append(nq_kv* kv, int32_t layer, int32_t batch, const int32_t* p
 size_t nq_attn_workspace_bytes(const nq_config* cfg, int32_t batch, int32_t max_pages) {
   if (nq_config_check(cfg) != NQ_OK || batch < 1 || max_pages < 1 || max_pages > kAttnMaxPages) return 0;
   const int S = attn_plan(batch, cfg->n_kv_heads, max_pages).S;
+  if (S < 1) return 0;
   return align256(static_cast<size_t>(batch) * cfg->n_heads * S * cfg->head_dim * 4) +
          align256(static_cast<size_t>(batch) * cfg->n_heads * S * 2 * 4);
 }
@@ -614,8 +616,11 @@ nq_status nq_attn_decode(const nq_kv* kv, int32_t layer, int32_t batch, const vo
   a.n_kv = kv->cfg.n_kv_heads;
   a.head_dim = kv->cfg.head_dim;
   const AttnPlan plan = attn_plan(batch, kv->cfg.n_kv_heads, max_pages);
+  if (plan.S < 1)
+    return fail(NQ_ERR_OUT_OF_RANGE, "batch %d x max_pages %d is beyond the attention kernels", batch, max_pages);
   a.splits = plan.S;
   a.per = plan.per;
+  a.dyn = plan.dyn;
   a.part_o = static_cast<float*>(workspace);
   const size_t o_bytes = align256(static_cast<size_t>(batch) * a.n_heads * a.splits * a.head_dim * 4);
   a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + o_bytes);

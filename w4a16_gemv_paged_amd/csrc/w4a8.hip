@@ -163,14 +163,14 @@ __global__ __launch_bounds__(1024) void gemv_w4a8_kernel(A8Params p) {
   auto load_scales = [&](int w0) {
     const int bi = w0 + col;
     const int g = ksi + p.ks * bi;
-    return __builtin_amdgcn_raw_buffer_load_b64(srs, (col < kA8Depth && bi < n_c) ? g * 32 + kb * 8 : sbytes, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b64(srs, (col < kA8Depth && bi < n_c) ? g * 32 + kb * 8 : sbytes, 0, kStreamOnce);
   };
   u32x2 swin = load_scales(0);
   u32x4 wv[kA8Depth];
 #pragma unroll
   for (int u = 0; u < kA8Depth; ++u) {
     const int g = ksi + p.ks * u;
-    wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, lane * 16, u < n_c ? g * kBlockBytes : wbytes, 0);
+    wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, lane * 16, u < n_c ? g * kBlockBytes : wbytes, kStreamOnce);
   }
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kA8Depth + 1));  // this wave's LDS copies have landed
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(1024) void gemv_w4a8_kernel(A8Params p) {
         scale_acc(acc, f, row_bcast2(swin, u));
         if (i + kA8Depth < n_c) {  // refill the slot just consumed
           const int gn = ksi + p.ks * (i + kA8Depth);
-          wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, lane * 16, gn * kBlockBytes, 0);
+          wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, lane * 16, gn * kBlockBytes, kStreamOnce);
         }
       }
     }

@@ -37,7 +37,7 @@ namespace nq {
 
 constexpr int kDepth = 7;                   // 1 KiB weight loads in flight per wave
 constexpr int kDmaBatch = 8;                // activation copies issued back to back per wave
-constexpr size_t kLdsX = 56 * 1024;         // LDS budget for staged activations and gain
+constexpr size_t kLdsX = 140 * 1024;        // LDS budget for staged activations and gain (of 160 KiB)
 
 struct GemvParams {
   const uint8_t* codes;
@@ -832,8 +832,29 @@ static hipError_t launch_stream_b(int batch, bool gain, int epi, size_t lds, hip
   }
 }
 
+// Lets a GEMV instance take more than the default 64 KiB of dynamic LDS (once per instance).
+template <int B, int EPI, bool GAIN>
+static hipError_t allow_gemv_lds() {
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_w4a16_kernel<B, EPI, GAIN>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  return e;
+}
+
 template <int B, bool GAIN>
 static hipError_t launch_gemv_e(int epi, dim3 grid, dim3 block, size_t lds, hipStream_t stream, const GemvParams& p) {
+  if (lds > 64 * 1024) {
+    hipError_t e = hipSuccess;
+    switch (epi) {
+      case NQ_EPI_STORE_F16: e = allow_gemv_lds<B, NQ_EPI_STORE_F16, GAIN>(); break;
+      case NQ_EPI_BIAS_F16: e = allow_gemv_lds<B, NQ_EPI_BIAS_F16, GAIN>(); break;
+      case NQ_EPI_RESIDUAL_F16: e = allow_gemv_lds<B, NQ_EPI_RESIDUAL_F16, GAIN>(); break;
+      case NQ_EPI_SWIGLU_F16: e = allow_gemv_lds<B, NQ_EPI_SWIGLU_F16, GAIN>(); break;
+      case NQ_EPI_STORE_F32: e = allow_gemv_lds<B, NQ_EPI_STORE_F32, GAIN>(); break;
+      case EPI_QKV_ROPE_KV: e = allow_gemv_lds<B, EPI_QKV_ROPE_KV, GAIN>(); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+  }
   switch (epi) {
     case NQ_EPI_STORE_F16: gemv_w4a16_kernel<B, NQ_EPI_STORE_F16, GAIN><<<grid, block, lds, stream>>>(p); break;
     case NQ_EPI_BIAS_F16: gemv_w4a16_kernel<B, NQ_EPI_BIAS_F16, GAIN><<<grid, block, lds, stream>>>(p); break;

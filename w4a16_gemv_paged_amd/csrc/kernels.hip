@@ -744,23 +744,27 @@ struct GemvShape {
   size_t lds;
 };
 
-// Launch shape, from a sweep of (tiles per workgroup, K-slices) on MI355X at
-// the decode shapes. Matrices with few tiles (T < 1024: the QKV, O and down
-// projections) split K so that each wave owns about 7 groups (at most 8
-// slices) and run one tile per workgroup below 256 tiles, two above. Matrices
-// with many tiles (gate/up, LM head) already fill the chip with workgroups:
-// two tiles x two K-slices at batch 1-3, eight tiles x one slice from batch 4,
-// where each loaded block feeds more matrix-core columns. The staged
-// activations (plus the gain) get at most kLdsX bytes; longer K is processed
-// in chunks.
+// Launch shape, from sweeps of (tiles per workgroup, K-slices) on MI355X at
+// the decode shapes and batches 1, 4 and 8. Matrices with few tiles
+// (T < 1024: the QKV, O and down projections) split K: two tiles per
+// workgroup from 256 tiles, each wave owning about 7 groups; one tile per
+// workgroup below that, with up to 8 slices of at least 3 groups each.
+// Matrices with many tiles (gate/up, LM head) already fill the chip with
+// workgroups: two tiles x two K-slices at batch 1-3, then one slice of four
+// (batch 4-5) or eight tiles (batch 6-8), where each loaded block feeds more
+// matrix-core columns. The staged activations (plus the gain) get at most
+// kLdsX bytes; longer K is processed in chunks.
 static GemvShape gemv_shape(int T, int G, int B, bool gain) {
   GemvShape s;
   if (T >= 1024) {
     s.ks = B >= 4 ? 1 : 2;
-    s.tpw = B >= 4 ? 8 : 2;
-  } else {
+    s.tpw = B >= 6 ? 8 : B >= 4 ? 4 : 2;
+  } else if (T >= 256) {
     s.ks = std::min(8, (G + 6) / 7);
-    s.tpw = T >= 256 ? 2 : 1;
+    s.tpw = 2;
+  } else {
+    s.ks = std::min(8, std::max(1, G / 3));
+    s.tpw = 1;
   }
   s.ks = std::max(1, std::min(s.ks, G));
   const int rows = B + (gain ? 1 : 0);

@@ -38,6 +38,8 @@ PEAK_HBM = 8.0e12
 GEMV_ROTATION = {(3584, 4608): 64, (3584, 3584): 82, (3584, 37888): 8, (18944, 3584): 16}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_gate_up_swiglu_7b_b1_pmc.md")
 KERNEL_SRC = os.path.join(ROOT, "w4a16_gemv_paged_amd", "csrc", "kernels.hip")
+DEVICE_HDR = os.path.join(ROOT, "w4a16_gemv_paged_amd", "csrc", "device.hpp")
+ATTN_MARK = b"// ============================================================== attention"
 
 
 def log(msg: str) -> None:
@@ -61,7 +63,13 @@ def step_weight_bytes(shape) -> int:
 
 
 def kernel_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the source the gate/up GEMV is built from: the GEMV part of
+    kernels.hip (everything before the attention section) and device.hpp."""
+    src = open(KERNEL_SRC, "rb").read()
+    cut = src.find(ATTN_MARK)
+    h = hashlib.sha256(src[:cut] if cut > 0 else src)
+    h.update(open(DEVICE_HDR, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():

@@ -37,12 +37,14 @@ namespace nq {
 
 constexpr int kDepth = 7;                   // 1 KiB weight loads in flight per wave
 constexpr int kDmaBatch = 8;                // activation copies issued back to back per wave
+constexpr int kGemvCUs = 256;               // MI355X compute units: one workgroup each in an even spread
 constexpr size_t kLdsX = 140 * 1024;        // LDS budget for staged activations and gain (of 160 KiB)
 
 struct GemvParams {
   const uint8_t* codes;
   const uint8_t* scales;
   int N, K, kind, head_dim, G, T, tpw, ks, ch, xrow;
+  int bal;  // tiles spread evenly over the grid (9 or 10 of 2368 over 256 workgroups), else tpw each
   const half_t* x;
   const half_t* gain;
   float eps;
@@ -101,8 +103,14 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
   const int nw = blockDim.x >> 6;
   const int col = lane & 15, kb = lane >> 4;
   const int tl = wave / p.ks, ksi = wave % p.ks;
-  const int t = static_cast<int>(blockIdx.x) * p.tpw + tl;
-  const bool tile_ok = t < p.T;  // wave-uniform
+  // this workgroup's tiles [t0, t1): tpw each, or an even share of the T tiles
+  // (at most tpw) so that no CU gets a second workgroup's worth of work
+  const int t0 = p.bal ? static_cast<int>(static_cast<int64_t>(blockIdx.x) * p.T / gridDim.x)
+                       : static_cast<int>(blockIdx.x) * p.tpw;
+  const int t1 = p.bal ? static_cast<int>((static_cast<int64_t>(blockIdx.x) + 1) * p.T / gridDim.x)
+                       : min(p.T, t0 + p.tpw);
+  const int t = t0 + tl;
+  const bool tile_ok = t < t1;  // wave-uniform
   const int xrow = p.xrow;       // halfs per staged row, a multiple of 512 (1 KiB)
   // LDS: [B] activation rows | gain row (GAIN) | zero block | red | ssq | lg
   half_t* xs = reinterpret_cast<half_t*>(smem);
@@ -123,8 +131,8 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
   if constexpr (EPI == EPI_QKV_ROPE_KV) {
     if (tid < items) {
       const int tl2 = tid / (B * 16), b = (tid / 16) % B, rr = tid & 15;
-      const int64_t tt = static_cast<int64_t>(blockIdx.x) * p.tpw + tl2;
-      if (tt < p.T) {
+      const int64_t tt = static_cast<int64_t>(t0) + tl2;
+      if (tt < t1) {
         const int64_t n = tile_row_logical(p.kind, p.N, p.head_dim, tt, rr);
         const int64_t np = tile_row_logical(p.kind, p.N, p.head_dim, tt, rr ^ 8);
         e_bias = static_cast<float>(p.bias[n]);
@@ -148,8 +156,8 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
   if constexpr (EPI == NQ_EPI_RESIDUAL_F16) {
     if (tid < items) {
       const int tl2 = tid / (B * 16), b = (tid / 16) % B, rr = tid & 15;
-      const int64_t tt = static_cast<int64_t>(blockIdx.x) * p.tpw + tl2;
-      if (tt < p.T) {
+      const int64_t tt = static_cast<int64_t>(t0) + tl2;
+      if (tt < t1) {
         const int64_t n = tile_row_logical(p.kind, p.N, p.head_dim, tt, rr);
         if (n < p.N) e_res = static_cast<const half_t*>(p.y)[b * static_cast<int64_t>(p.N) + n];
       }
@@ -320,8 +328,8 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
 
   for (int i = tid; i < items; i += blockDim.x) {
     const int tl2 = i / (B * 16), b = (i / 16) % B, rr = i & 15;
-    const int64_t tt = static_cast<int64_t>(blockIdx.x) * p.tpw + tl2;
-    if (tt >= p.T) continue;
+    const int64_t tt = static_cast<int64_t>(t0) + tl2;
+    if (tt >= t1) continue;
     float rsb = 1.0f;
     if constexpr (GAIN) {
       float v = 0.0f;
@@ -421,8 +429,8 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
         int bi = 0x7fffffff;
         bool nan = false;
         for (int tl2 = 0; tl2 < p.tpw; ++tl2) {
-          const int64_t tt = static_cast<int64_t>(blockIdx.x) * p.tpw + tl2;
-          if (tt >= p.T) break;
+          const int64_t tt = static_cast<int64_t>(t0) + tl2;
+          if (tt >= t1) break;
           for (int rr = 0; rr < 16; ++rr) {
             const float v = lg[(tl2 * B + b) * 16 + rr];
             const int n = static_cast<int>(tile_row_logical(p.kind, p.N, p.head_dim, tt, rr));
@@ -740,7 +748,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvPara
 }
 
 struct GemvShape {
-  int tpw, ks, ch, xrow, threads;
+  int tpw, ks, ch, xrow, threads, grid, bal;
   size_t lds;
 };
 
@@ -752,13 +760,23 @@ struct GemvShape {
 // Matrices with many tiles (gate/up, LM head) already fill the chip with
 // workgroups: two tiles x two K-slices at batch 1-3, then one slice of four
 // (batch 4-5) or eight tiles (batch 6-8), where each loaded block feeds more
-// matrix-core columns. The staged activations (plus the gain) get at most
+// matrix-core columns. The workgroup count matters as much: with 264
+// workgroups of 9 tiles (8 CUs holding two) gate/up took 28.5 us against 17
+// us. From batch 4 the tiles are therefore spread evenly over one workgroup
+// per CU (9 or 10 tiles of gate/up each; batch 8 22.6 against 28.3 us with 8
+// tiles per workgroup). The staged activations (plus the gain) get at most
 // kLdsX bytes; longer K is processed in chunks.
 static GemvShape gemv_shape(int T, int G, int B, bool gain) {
   GemvShape s;
-  if (T >= 1024) {
-    s.ks = B >= 4 ? 1 : 2;
-    s.tpw = B >= 6 ? 8 : B >= 4 ? 4 : 2;
+  s.bal = 0;
+  if (T >= 1024 && B >= 4) {
+    s.ks = 1;
+    s.tpw = std::min(16, (T + kGemvCUs - 1) / kGemvCUs);  // at most 16 waves per workgroup
+    s.grid = std::max(kGemvCUs, (T + s.tpw - 1) / s.tpw);  // every share holds at most tpw tiles
+    s.bal = 1;
+  } else if (T >= 1024) {
+    s.ks = 2;
+    s.tpw = 2;
   } else if (T >= 256) {
     s.ks = std::min(8, (G + 6) / 7);
     s.tpw = 2;
@@ -772,6 +790,7 @@ static GemvShape gemv_shape(int T, int G, int B, bool gain) {
   s.ch = G <= fit ? G : std::max(s.ks, fit / s.ks * s.ks);
   s.xrow = (s.ch * 128 + 511) / 512 * 512;
   s.threads = s.tpw * s.ks * 64;
+  if (!s.bal) s.grid = (T + s.tpw - 1) / s.tpw;
   const int nw = s.tpw * s.ks;
   s.lds = static_cast<size_t>(rows) * s.xrow * 2 + 256 + static_cast<size_t>(nw) * B * 16 * 4 + nw * B * 4 +
           static_cast<size_t>(s.tpw) * B * 16 * 4;
@@ -781,8 +800,7 @@ static GemvShape gemv_shape(int T, int G, int B, bool gain) {
 int gemv_grid_size(int32_t N, int32_t K, int32_t batch) {
   const int T = static_cast<int>(tiles_of(N));
   if (stream_plan(T, K / kGroup, batch, true).ok) return kStreamGroups;
-  const GemvShape sh = gemv_shape(T, K / kGroup, batch, true);
-  return (T + sh.tpw - 1) / sh.tpw;
+  return gemv_shape(T, K / kGroup, batch, true).grid;
 }
 
 // Lets a streaming kernel take more than the default 64 KiB of dynamic LDS (once per kernel).
@@ -904,6 +922,7 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
   const GemvShape sh = gemv_shape(p.T, p.G, a.batch, a.norm_gain != nullptr);
   p.tpw = sh.tpw;
   p.ks = sh.ks;
+  p.bal = sh.bal;
   p.ch = sh.ch;
   p.xrow = sh.xrow;
   p.codes = static_cast<const uint8_t*>(a.packed);
@@ -938,7 +957,7 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
     p.xrow = sp.xrow;
     return launch_stream_b(a.batch, a.norm_gain != nullptr, a.epi, sp.lds, stream, p);
   }
-  const dim3 grid((p.T + p.tpw - 1) / p.tpw), block(sh.threads);
+  const dim3 grid(sh.grid), block(sh.threads);
   return launch_gemv_b(a.batch, a.norm_gain != nullptr, a.epi, grid, block, sh.lds, stream, p);
 }
 

@@ -983,15 +983,16 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
 // Scratch", FAQ on the barrier inside a warp-id branch). When one workgroup
 // covers the whole context it writes the output; otherwise workgroups write
 // (max, sum, output) partials and the combine kernel merges them with the
-// log-sum-exp rule. The split follows the actual lengths, not the table
-// width: every workgroup of a fixed grid of S per KV head reads the lengths,
-// takes per = the page count per split that spreads all sequences' pages over
-// the grid, and finds its (sequence, split) from the running sum of the
-// sequences' split counts ceil(pages_b / per). A ragged batch then gives every
-// workgroup about the same number of pages, and the grid (hence a captured
-// graph) does not depend on the lengths. Workgroups are 4 waves, so that three of them fit on a CU
-// at the kernel's register count: 12 waves per CU where one 8-wave workgroup
-// gives 8, and a finer grain for ragged batches.
+// log-sum-exp rule. A batch of one takes fixed splits of one page per wave.
+// Larger batches split by the actual lengths, not the table width: every
+// workgroup of a fixed grid of S per KV head reads the lengths, takes per =
+// the page count per split that spreads all sequences' pages over the grid,
+// and finds its (sequence, split) from the running sum of the sequences'
+// split counts ceil(pages_b / per). A ragged batch then gives every workgroup
+// about the same number of pages, and the grid (hence a captured graph) does
+// not depend on the lengths. Workgroups are 4 waves, so that three of them
+// fit on a CU at the kernel's register count: 12 waves per CU where one
+// 8-wave workgroup gives 8, and a finer grain for ragged batches.
 
 constexpr int kAttnWaves = 4;
 constexpr int kMaxPagesPerWave = 128;  // a split holds at most kAttnWaves * 128 pages

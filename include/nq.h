@@ -344,7 +344,8 @@ void nq_kv_free(nq_kv* kv);
 
 /* ----------------------------------------------------- decode attention */
 
-/* Scratch bytes nq_attn_decode needs for its split-K partials. */
+/* Scratch bytes nq_attn_decode needs for its split-K partials; 0 for an invalid
+ * configuration or a batch and table width beyond the kernels (see below). */
 size_t nq_attn_workspace_bytes(const nq_config* cfg, int32_t batch, int32_t max_pages);
 
 /*

@@ -200,6 +200,34 @@ def test_config_check_and_sizes():
     assert nq.nq_attn_workspace_bytes(cfg, 64, 32768) == 0
 
 
+def test_attention_split_plan_sizes():
+    """The split plan behind nq_attn_workspace_bytes (partials are
+    [B][n_heads][S][d] and [B][n_heads][S][2] floats, each 256-byte aligned):
+    batch 1 takes fixed splits of 4 pages (one per wave) while they number at
+    most 768 / n_kv; larger batches split by length over min(768 / n_kv,
+    B * ceil(pages / 4)) workgroups per KV head, at least B + 1; beyond 1024
+    workgroups of 512 pages, or 64 sequences, nothing."""
+    import synth
+    cfg = nq.NQConfig.from_shape(synth.QWEN7B, 8, 32768)
+    nh, d = cfg.n_heads, cfg.head_dim
+    a256 = lambda n: (n + 255) // 256 * 256
+
+    def ws(batch, S):
+        return a256(batch * nh * S * d * 4) + a256(batch * nh * S * 2 * 4)
+
+    assert nq.nq_attn_workspace_bytes(cfg, 1, 4) == ws(1, 1)
+    assert nq.nq_attn_workspace_bytes(cfg, 1, 52) == ws(1, 13)
+    assert nq.nq_attn_workspace_bytes(cfg, 1, 768) == ws(1, 192)
+    assert nq.nq_attn_workspace_bytes(cfg, 1, 769) == ws(1, 192)    # past 192 fixed splits: by length
+    assert nq.nq_attn_workspace_bytes(cfg, 1, 2048) == ws(1, 192)
+    assert nq.nq_attn_workspace_bytes(cfg, 2, 8) == ws(2, 4)        # 2 * ceil(8 / 4) splits
+    assert nq.nq_attn_workspace_bytes(cfg, 8, 3) == ws(8, 1)        # tables of at most 4 pages: unsplit
+    assert nq.nq_attn_workspace_bytes(cfg, 8, 2048) == ws(8, 192)
+    assert nq.nq_attn_workspace_bytes(cfg, 8, 32768) == ws(8, 520)  # 8 * 32768 / 512 + 8: no split over 512 pages
+    assert nq.nq_attn_workspace_bytes(cfg, 65, 64) == 0
+    assert nq.nq_attn_workspace_bytes(cfg, 64, 32768) == 0
+
+
 def test_rope_table_matches_definition():
     import synth
     cfg = nq.NQConfig.from_shape(synth.QWEN7B, 1, 40000)

@@ -178,10 +178,11 @@ def test_batch8_logits_against_oracle(tiny):
 
 
 def test_split_attention_long_context(tiny):
-    """Batch 1 over 64-page tables: attention splits the pages over 8
-    workgroups whose partials the combine kernel merges. 200-token prompt
-    (13 pages at the end: two splits hold pages, the rest are empty). Logits and
-    tokens against the oracle; graph replay equals eager bitwise."""
+    """Batch 1 over 64-page tables: attention splits the pages over 16
+    workgroups per KV head (4 pages each, one per wave) whose partials the
+    combine kernel merges. 200-token prompt (13-14 pages in use: four splits
+    hold pages, the rest are empty). Logits and tokens against the oracle;
+    graph replay equals eager bitwise."""
     om, dm = tiny
     prompt = synth.prompt_ids(200, SHAPE.vocab, seed=60)
     say("tiny long-context eager run")

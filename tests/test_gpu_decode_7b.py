@@ -45,8 +45,9 @@ def model7b():
 def run7b(model7b):
     dm, head = model7b
     prompt = synth.prompt_ids(PROMPT, SHAPE.vocab, seed=2)
-    # 52-page tables as in the timed run: attention splits the pages over 7
-    # workgroups (all but the first empty at this length) and merges them
+    # 52-page tables as in the timed run: attention splits the pages over 13
+    # workgroups per KV head (all but the first empty at this length) and
+    # merges them
     pt, total = synth.decode_page_tables(1, 52, seed=3, spare_pages=2)
     out = {}
     for graph in (False, True):

@@ -38,7 +38,8 @@ namespace nq {
 constexpr int kDepth = 7;                   // 1 KiB weight loads in flight per wave
 constexpr int kDmaBatch = 8;                // activation copies issued back to back per wave
 constexpr int kGemvCUs = 256;               // MI355X compute units: one workgroup each in an even spread
-constexpr size_t kLdsX = 140 * 1024;        // LDS budget for staged activations and gain (of 160 KiB)
+constexpr size_t kLdsMax = 160 * 1024;      // LDS of a workgroup on gfx950
+constexpr size_t kLdsX = 152 * 1024;        // LDS budget for staged activations and gain
 
 struct GemvParams {
   const uint8_t* codes;
@@ -786,14 +787,20 @@ static GemvShape gemv_shape(int T, int G, int B, bool gain) {
   }
   s.ks = std::max(1, std::min(s.ks, G));
   const int rows = B + (gain ? 1 : 0);
-  const int fit = static_cast<int>(kLdsX / (static_cast<size_t>(rows) * 256)) / 4 * 4;  // whole 1 KiB blocks
-  s.ch = G <= fit ? G : std::max(s.ks, fit / s.ks * s.ks);
+  const int nw = s.tpw * s.ks;
+  // zero block, cross-wave partials, sums of squares, argmax logits
+  const size_t extras = 256 + static_cast<size_t>(nw) * B * 16 * 4 + static_cast<size_t>(nw) * B * 4 +
+                        static_cast<size_t>(s.tpw) * B * 16 * 4;
+  const size_t budget = std::min(kLdsX, kLdsMax - extras);
+  const int fit = static_cast<int>(budget / (static_cast<size_t>(rows) * 256)) / 4 * 4;  // whole 1 KiB blocks
+  // a chunk's groups are dealt out to the K-slices afresh, so it need not be a
+  // multiple of them: at batch 8 the down projection's 148 groups take two
+  // chunks of 76 and 72 (19.3 us) instead of three of 64, 64 and 20 (20.7 us)
+  s.ch = G <= fit ? G : std::max(4, fit);
   s.xrow = (s.ch * 128 + 511) / 512 * 512;
   s.threads = s.tpw * s.ks * 64;
   if (!s.bal) s.grid = (T + s.tpw - 1) / s.tpw;
-  const int nw = s.tpw * s.ks;
-  s.lds = static_cast<size_t>(rows) * s.xrow * 2 + 256 + static_cast<size_t>(nw) * B * 16 * 4 + nw * B * 4 +
-          static_cast<size_t>(s.tpw) * B * 16 * 4;
+  s.lds = static_cast<size_t>(rows) * s.xrow * 2 + extras;
   return s;
 }
 
@@ -858,7 +865,7 @@ static hipError_t launch_stream_b(int batch, bool gain, int epi, size_t lds, hip
 template <int B, int EPI, bool GAIN>
 static hipError_t allow_gemv_lds() {
   static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_w4a16_kernel<B, EPI, GAIN>),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
   return e;
 }
 

@@ -14,8 +14,15 @@ groups), so that each group's product is an exact integer sum:
   q  = clamp( round_half_even( float32(x) / s ), -127, 127 ),  q = 0 if s == 0
   y[b][n] = sum_g  sw[n][g] * s[b][g] * sum_{k in g} qw[n][k] * q[b][k]
 
-The decisions that make integers (the quotient x / s) are taken in float32,
-the precision the kernel takes them in; the rest is float64.
+The activation quantiser is defined in binary32 throughout (READING): its
+scale is itself a binary32 quotient, fl32(fl32(max|x|) / 127), and the code
+decision is the correctly rounded binary32 quotient of the two binary32
+operands fl32(x) and s, rounded half to even. (The weight rule of
+``quant.py`` takes its quotient in binary64 because its scale is an fp16
+number and exact ties of w / s16 must reach round-half-even intact.) A
+binary64 quotient would decide differently only when the exact quotient lies
+within half a binary32 ulp of a tie; tests/golden/a8_hand.json pins one such
+case (x = max / 2). The products and sums after the decision are float64.
 """
 from __future__ import annotations
 

@@ -1,15 +1,22 @@
 """GPU decode parity at the full Qwen2.5-Coder-7B shape (28 layers, hidden 3584,
-28/4 heads of dim 128, vocab 152064), the launch configuration bench.py times.
+28/4 heads of dim 128, vocab 152064), in the launch configuration bench.py times.
 
-The full oracle run of a 7B-shaped model is too slow for a test, so the run is
-short (24 prompt tokens + 8 generated) and checked on samples the oracle can
-afford: three layers recomputed teacher-forced from the GPU's own layer inputs
-(first, middle, last), and the LM head + greedy choice recomputed from the
-GPU's final hidden state at every generated step over the full vocabulary.
-The chunked prefill is checked the same way on the 512-token prompt that the
-benchmark's time to first token uses (one chunk of 512 rows). Batch 8 (ragged
-prompts, the attention split by length and the even GEMV tile spread) is
-checked against each of its sequences run at batch 1."""
+A full oracle run of a 7B-shaped model is too slow for a test, so the runs are
+checked on samples the oracle can afford: three layers (first, middle, last)
+recomputed teacher-forced from the GPU's own layer inputs at every position,
+and the LM head + greedy choice recomputed from the GPU's final hidden state
+over the full vocabulary at every generated step.
+
+* A short run (24 prompt tokens + 8 generated), eager and as graph replays.
+* The benchmark's configuration: the 512-token prompt of bench.py through the
+  chunked prefill (one chunk), then graph-replayed decode steps at contexts
+  513-592 over the benchmark's 52-page table, where attention splits the pages
+  over 13 workgroups per KV head (9-10 of them live) and the combine kernel
+  merges them.
+* Batch 8 (ragged prompts of 128-512 tokens, seed 4, through the prefill, then
+  31 graph-replayed steps; attention split by length, the even GEMV tile
+  spread), each sequence against the oracle the same way, and against the same
+  sequence run alone at batch 1."""
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -71,26 +78,21 @@ def test_7b_graph_equals_eager(run7b):
     np.testing.assert_array_equal(graph["layer_out"].view(np.uint16), eager["layer_out"].view(np.uint16))
 
 
-def test_7b_layers_teacher_forced(run7b):
+def test_7b_layers_teacher_forced(run7b, oracle_layers):
     prompt, head, gpu, _ = run7b
     fed = list(prompt) + list(gpu["tokens"][0][:-1])
     lo = gpu["layer_out"][:, :, 0]                                   # [T, L, H]
-    dims = Dims(SHAPE.hidden, SHAPE.intermediate, SHAPE.n_heads, SHAPE.n_kv_heads, SHAPE.head_dim, SHAPE.vocab)
-    with ThreadPoolExecutor(len(LAYERS)) as ex:
-        layers = list(ex.map(lambda l: OracleLayer(synth.layer_params(SHAPE, l, seed=0), quant=quantize_rows), LAYERS))
-    for li, L in zip(LAYERS, layers):
+    for li, L in oracle_layers:
         say("oracle layer", li)
         x = head["embed"][np.array(fed)] if li == 0 else lo[:, li - 1]
-        ref = layer_causal(L, dims, x)
+        ref = layer_causal(L, _dims(), x)
         errs = [rel_inf(lo[t, li], ref[t]) for t in range(len(fed))]
         assert max(errs) < TOL_LAYER, (li, max(errs))
-        L.drop_cache()
 
 
-def test_7b_head_logits_and_tokens(run7b):
+def test_7b_head_logits_and_tokens(run7b, lm_dequant):
     prompt, head, gpu, _ = run7b
-    q, s = quantize_rows(head["lm_head"])
-    w = oracle.dequantize_w4(q, s)
+    w = lm_dequant
     hfin = gpu["layer_out"][:, -1, 0]                               # [T, H] after the last layer
     x = oracle.rmsnorm(hfin, head["g_final"], 1e-6).astype(np.float64)
     steps = range(PROMPT - 1, PROMPT - 1 + GEN)
@@ -128,29 +130,130 @@ def prefill7b(model7b):
     return prompt, head, out
 
 
-def test_7b_prefill_layers_teacher_forced(prefill7b):
+def test_7b_prefill_layers_teacher_forced(prefill7b, oracle_layers):
     prompt, head, gpu = prefill7b
     lo = gpu["layer_out"]                                            # [L, T, H]
-    dims = Dims(SHAPE.hidden, SHAPE.intermediate, SHAPE.n_heads, SHAPE.n_kv_heads, SHAPE.head_dim, SHAPE.vocab)
-    for li in LAYERS:
+    for li, L in oracle_layers:
         say("oracle prefill layer", li)
-        L = OracleLayer(synth.layer_params(SHAPE, li, seed=0), quant=quantize_rows)
         x = head["embed"][np.array(prompt)] if li == 0 else lo[li - 1]
-        ref = layer_causal(L, dims, x)
+        ref = layer_causal(L, _dims(), x)
         errs = [rel_inf(lo[li, t], ref[t]) for t in range(PF_PROMPT)]
         assert max(errs) < TOL_LAYER, (li, int(np.argmax(errs)), max(errs))
-        L.drop_cache()
 
 
-def test_7b_prefill_head(prefill7b):
+def test_7b_prefill_head(prefill7b, lm_dequant):
     prompt, head, gpu = prefill7b
-    q, s = quantize_rows(head["lm_head"])
     x = oracle.rmsnorm(gpu["layer_out"][-1, -1], head["g_final"], 1e-6).astype(np.float64)
-    z = oracle.dequantize_w4(q, s) @ x
+    z = lm_dequant @ x
     assert rel_inf(gpu["logits"], z) < TOL_LOGITS
     top2 = np.sort(z)[-2:]
     if top2[1] - top2[0] > MARGIN:
         assert gpu["next"] == oracle.argmax_lowest(z)
+
+
+# ---------------------------------------------------------------- the benchmark's configuration
+
+BENCH_PROMPT, BENCH_GEN, BENCH_PAGES = 512, 81, 52
+
+
+def _dims():
+    return Dims(SHAPE.hidden, SHAPE.intermediate, SHAPE.n_heads, SHAPE.n_kv_heads, SHAPE.head_dim, SHAPE.vocab)
+
+
+def _oracle_layers(ids):
+    def build(l):
+        L = OracleLayer(synth.layer_params(SHAPE, l, seed=0), quant=quantize_rows)
+        for name in ("qkv", "o", "gu", "d"):   # dequantise once, before threads share the layer
+            L.w(name)
+        return L
+
+    with ThreadPoolExecutor(len(ids)) as ex:
+        return list(zip(ids, ex.map(build, ids)))
+
+
+@pytest.fixture(scope="module")
+def oracle_layers():
+    return _oracle_layers(LAYERS)
+
+
+def _layer_inputs(head, li, fed, pf_lo, dec_lo):
+    """Layer li's input at every position: the embedding of the fed token for
+    layer 0, else the GPU's own layer li-1 output (prefill rows, then decode
+    steps)."""
+    if li == 0:
+        return head["embed"][np.array(fed)]
+    return np.concatenate([pf_lo[li - 1], dec_lo[:, li - 1]], axis=0)
+
+
+def _check_layers(layers, head, fed, pf_lo, dec_lo, tag):
+    """Teacher-forced layers against the GPU outputs at every position."""
+    P = pf_lo.shape[1]
+    for li, L in layers:
+        ref = layer_causal(L, _dims(), _layer_inputs(head, li, fed, pf_lo, dec_lo))
+        got = np.concatenate([pf_lo[li], dec_lo[:, li]], axis=0)
+        errs = [rel_inf(got[t], ref[t]) for t in range(len(fed))]
+        assert max(errs) < TOL_LAYER, (tag, li, int(np.argmax(errs)), max(errs))
+        assert max(errs[P:]) < TOL_LAYER
+
+
+def _check_head(w_lm, head, h_final, logits, tokens, tag):
+    """Full-vocabulary logits within TOL_LOGITS; tokens equal wherever the
+    oracle's top-1 margin exceeds MARGIN. Returns the number of such steps."""
+    x = oracle.rmsnorm(h_final, head["g_final"], 1e-6).astype(np.float64)
+    z = x @ w_lm.T
+    clear = 0
+    for i in range(len(tokens)):
+        assert rel_inf(logits[i], z[i]) < TOL_LOGITS, (tag, i, rel_inf(logits[i], z[i]))
+        top2 = np.sort(z[i])[-2:]
+        if top2[1] - top2[0] > MARGIN:
+            clear += 1
+            assert tokens[i] == oracle.argmax_lowest(z[i]), (tag, i)
+    return clear
+
+
+@pytest.fixture(scope="module")
+def lm_dequant(model7b):
+    dm, head = model7b
+    q, s = quantize_rows(head["lm_head"])
+    return oracle.dequantize_w4(q, s)
+
+
+@pytest.fixture(scope="module")
+def bench_run(model7b):
+    dm, head = model7b
+    prompt = synth.prompt_ids(BENCH_PROMPT, SHAPE.vocab, seed=2)       # bench.py's prompt
+    pt, total = synth.decode_page_tables(1, BENCH_PAGES, seed=3, spare_pages=2)
+    kv = KVCache(dm, total, poison=True)
+    st = Stepper(dm, kv, pt, want_logits=True, want_layers=True)
+    stream = torch.cuda.Stream()
+    say("7B benchmark configuration: prefill", BENCH_PROMPT, "then", BENCH_GEN - 1, "graph replays")
+    with torch.cuda.stream(stream):
+        r = run_greedy(st, [prompt], BENCH_GEN, use_graph=True, stream=stream, record_logits=True,
+                       record_layers=True, prefill_chunk=BENCH_PROMPT)
+    torch.cuda.synchronize()
+    st.close()
+    kv.close()
+    return prompt, head, r
+
+
+def test_7b_bench_config_layers_teacher_forced(bench_run, oracle_layers):
+    prompt, head, r = bench_run
+    toks = r["tokens"][0]
+    fed = list(prompt) + list(toks[:-1])                           # 512 prompt tokens + 80 decode inputs
+    pf_lo = r["prefill_layer_out"][0]                              # [L, 512, H]
+    dec_lo = r["layer_out"][:, :, 0]                               # [80, L, H], positions 512..591
+    assert dec_lo.shape[0] == BENCH_GEN - 1 and len(fed) == BENCH_PROMPT + BENCH_GEN - 1
+    say("oracle layers", LAYERS, "over", len(fed), "positions")
+    _check_layers(oracle_layers, head, fed, pf_lo, dec_lo, "bench")
+
+
+def test_7b_bench_config_head_logits_and_tokens(bench_run, lm_dequant):
+    prompt, head, r = bench_run
+    toks = r["tokens"][0]
+    h_fin = np.concatenate([r["prefill_layer_out"][0][-1][-1:], r["layer_out"][:, -1, 0]], axis=0)
+    logits = np.concatenate([r["prefill_logits"][:1], r["logits"][:, 0]], axis=0)
+    clear = _check_head(lm_dequant, head, h_fin, logits, toks, "bench")
+    assert clear >= BENCH_GEN // 2
 
 
 # ---------------------------------------------------------------- batch 8
@@ -176,9 +279,10 @@ def batch8_runs(model7b):
     say("7B batch 8, prompt lengths", lens.tolist())
     pt8, total8 = synth.decode_page_tables(8, max_pages, seed=3, spare_pages=2)
     kv = KVCache(dm, total8, poison=True)
-    st = Stepper(dm, kv, pt8, want_logits=True)
+    st = Stepper(dm, kv, pt8, want_logits=True, want_layers=True)
     with torch.cuda.stream(stream):
-        r8 = run_greedy(st, prompts, B8_GEN, use_graph=True, stream=stream, record_logits=True, prefill_chunk=512)
+        r8 = run_greedy(st, prompts, B8_GEN, use_graph=True, stream=stream, record_logits=True,
+                        record_layers=True, prefill_chunk=512)
     torch.cuda.synchronize()
     st.close()
     kv.close()
@@ -194,11 +298,38 @@ def batch8_runs(model7b):
         torch.cuda.synchronize()
         st.close()
         kv.close()
-    return lens, r8, r1
+    return lens, prompts, head, r8, r1
+
+
+def test_7b_batch8_layers_teacher_forced(batch8_runs, oracle_layers):
+    """Each sequence of the batch-8 run: layers 0, 13 and 27 recomputed by the
+    oracle from the GPU's own inputs at all of its positions (prompt rows from
+    the prefill, then the 31 decode steps)."""
+    lens, prompts, head, r8, _ = batch8_runs
+
+    def one(b):
+        toks = r8["tokens"][b]
+        fed = list(prompts[b]) + list(toks[:-1])
+        _check_layers(oracle_layers, head, fed, r8["prefill_layer_out"][b], r8["layer_out"][:, :, b], ("b8", b))
+        say("sequence", b, "layers checked over", len(fed), "positions")
+
+    say("oracle layers of the 8 sequences")
+    with ThreadPoolExecutor(4) as ex:
+        list(ex.map(one, range(8)))
+
+
+def test_7b_batch8_head_logits_and_tokens(batch8_runs, lm_dequant):
+    lens, prompts, head, r8, _ = batch8_runs
+    clear = 0
+    for b in range(8):
+        h_fin = np.concatenate([r8["prefill_layer_out"][b][-1][-1:], r8["layer_out"][:, -1, b]], axis=0)
+        logits = np.concatenate([r8["prefill_logits"][b:b + 1], r8["logits"][:, b]], axis=0)
+        clear += _check_head(lm_dequant, head, h_fin, logits, r8["tokens"][b], ("b8", b))
+    assert clear >= 8 * B8_GEN // 2
 
 
 def test_7b_batch8_matches_batch1(batch8_runs):
-    lens, r8, r1 = batch8_runs
+    lens, prompts, head, r8, r1 = batch8_runs
     compared = 0
     for b in range(8):
         t8, t1 = r8["tokens"][b], r1[b]["tokens"][0]

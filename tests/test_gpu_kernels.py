@@ -136,6 +136,26 @@ def test_gemv_norm_bias_residual_swiglu(batch):
     assert rel_inf(host(ya), ref) < TOL_LAYER
 
 
+@pytest.mark.parametrize("batch", [4, 5, 8])
+def test_gemv_norm_gain_multi_chunk(batch):
+    """The RMSNorm prologue when the staged activation rows and the gain (B + 1
+    rows of K = 18944) exceed the LDS budget and are staged in several chunks:
+    each chunk reloads the gain, the sums of squares accumulate across chunks,
+    and the last chunk is not a multiple of the K-slices."""
+    K, N = 18944, 512
+    rng = np.random.default_rng(31)
+    h = (rng.standard_normal((batch, K)) * 3).astype(F16)
+    g = (1 + 0.02 * rng.standard_normal(K)).astype(F16)
+    w = synth.gemv_weight(K, N, seed=32)
+    b = (0.02 * rng.standard_normal(N)).astype(F16)
+    qo, so = oracle.quantize_w4(w)
+    xh = oracle.rmsnorm(h, g, 1e-6)
+    say("gemv norm gain multi-chunk", batch)
+    y = torch.empty(batch, N, dtype=torch.float16, device="cuda")
+    nq.nq_gemv_w4a16(_packed_dev(w), N, K, 0, 0, batch, dev(h), dev(g), 1e-6, dev(b), y, nq.NQ_EPI_BIAS_F16)
+    assert rel_inf(host(y), oracle.gemv_w4a16(qo, so, xh, b).astype(F16)) < TOL_LAYER
+
+
 def test_gemv_rejects_bad_arguments():
     w = synth.gemv_weight(256, 32, seed=9)
     p = _packed_dev(w)

@@ -32,6 +32,22 @@ def test_quantize_a8_hand_fixture():
             assert abs(float(s[0, gi]) - grp["scale_approx"]) < 1e-9
 
 
+def test_quantize_a8_decision_is_binary32():
+    """The code decision is the binary32 quotient rounded half to even: at
+    x = max / 2 the exact quotient is just below 63.5, its binary32 rounding is
+    63.5, and the code is the even neighbour 64 (a binary64 decision gives 63)."""
+    from fractions import Fraction
+    a, x = np.float16(1.884765625), np.float16(0.9423828125)
+    row = np.zeros((1, 128), np.float16)
+    row[0, 0], row[0, 1] = a, x
+    q, s = quantize_a8(row)
+    exact = Fraction(float(x)) / Fraction(float(s[0, 0]))
+    assert Fraction(63) < exact < Fraction(127, 2)
+    assert np.float32(np.float32(x) / s[0, 0]) == np.float32(63.5)
+    assert q[0, 1] == 64 and q[0, 0] == 127
+    assert int(np.rint(float(x) / float(s[0, 0]))) == 63
+
+
 def test_quantize_a8_bound_range_and_symmetry():
     rng = np.random.default_rng(0)
     x = (rng.standard_normal((5, 1024)) * np.repeat(rng.uniform(0.01, 20, (5, 8)), 128, axis=1)).astype(np.float16)

@@ -281,7 +281,10 @@ def run_greedy(st: Stepper, prompts, n_gen: int, use_graph: bool = False, stream
     With ``prefill_chunk``, each prompt goes through ``nq_prefill`` instead
     (chunks of that many tokens), which yields its first generated token and
     position; the remaining n_gen - 1 tokens come from decode steps. Logits and
-    layer outputs are then recorded for the decode steps only."""
+    layer outputs of the decode steps are recorded as above; ``record_layers``
+    also returns each sequence's prefill layer outputs [L][P_b][H]
+    (``prefill_layer_out``) and ``record_logits`` the logits of the prompt's
+    last row (``prefill_logits`` [B][V])."""
     if prefill_chunk:
         return _run_prefilled(st, prompts, n_gen, use_graph, stream, record_logits, record_layers, prefill_chunk)
     B = st.batch
@@ -325,9 +328,18 @@ def _run_prefilled(st: Stepper, prompts, n_gen, use_graph, stream, record_logits
     if stream is None:
         stream = torch.cuda.current_stream()
     pf = Prefill(st.model, st.kv, chunk)
+    cfg = st.model.cfg
+    pf_layers, pf_logits = [], []
     for b in range(B):
+        lo = (torch.empty(cfg.layers, len(prompts[b]), cfg.hidden, dtype=torch.float16, device=st.model.device)
+              if record_layers else None)
+        lg = torch.empty(cfg.vocab, dtype=torch.float32, device=st.model.device) if record_logits else None
         pf.run(prompts[b], st.page_table[b], 0, next_token=st.tokens[b:b + 1], pos_out=st.pos[b:b + 1],
-               stream=stream)
+               logits=lg, layer_out=lo, stream=stream)
+        if record_layers:
+            pf_layers.append(lo.cpu().numpy())
+        if record_logits:
+            pf_logits.append(lg.cpu().numpy())
     pf.check(stream)
     gen = [[int(t)] for t in st.tokens.cpu().numpy()]
     logits, layers = [], []
@@ -349,6 +361,8 @@ def _run_prefilled(st: Stepper, prompts, n_gen, use_graph, stream, record_logits
     out = {"tokens": np.array(gen, np.int64)}
     if record_logits:
         out["logits"] = np.array(logits)
+        out["prefill_logits"] = np.array(pf_logits)
     if record_layers:
         out["layer_out"] = np.array(layers)
+        out["prefill_layer_out"] = pf_layers
     return out

@@ -22,8 +22,10 @@
  *   - Arguments are validated before anything is enqueued, so a call that
  *     fails validation has no side effects. No C++ exception crosses the ABI.
  *   - Device memory is owned by the caller (the library never allocates device
- *     memory); handles store raw device pointers, which must stay valid while
- *     the handle (and any graph captured from it) is in use.
+ *     memory; the one device buffer it owns is the fixed scratch array of
+ *     nq_attn_decode_static, part of the loaded code object); handles store raw
+ *     device pointers, which must stay valid while the handle (and any graph
+ *     captured from it) is in use.
  *   - "stream" is a hipStream_t passed as void*. Nothing in the decode step
  *     synchronises; results are ready when the stream is.
  *   - Device pointers that the kernels read with 128-bit loads (packed weights,
@@ -373,6 +375,27 @@ nq_status nq_attn_decode(const nq_kv* kv, int32_t layer, int32_t batch, const vo
                          const int32_t* page_table, int32_t max_pages, const int32_t* lens,
                          void* out, void* workspace, size_t ws_bytes, int32_t* err_flag,
                          void* stream);
+
+/*
+ * The same split-K paged decode attention with no workspace argument and no
+ * allocation, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results and errors are those of nq_attn_decode. The split
+ * partials live in a library-owned device array of NQ_ATTN_SCRATCH_BYTES
+ * (24 MiB) on each GPU, held until the process ends; its address is looked up
+ * on the first call on a device. A call whose nq_attn_workspace_bytes(cfg,
+ * batch, max_pages) exceeds NQ_ATTN_SCRATCH_BYTES fails with
+ * NQ_ERR_OUT_OF_RANGE before anything is enqueued (batch 1 covers any table
+ * width; at the 7B shape, 28 heads of 128, batch 8 covers up to 192 splits).
+ * Every call on one GPU shares that array and leaves its partials there: calls
+ * that may overlap on one GPU (other streams, other threads) race, and the
+ * caller must order them. Nothing in the array needs to start at zero (every
+ * split writes its partial row before the merge reads it).
+ */
+#define NQ_ATTN_SCRATCH_BYTES (24u << 20)
+nq_status nq_attn_decode_static(const nq_kv* kv, int32_t layer, int32_t batch, const void* q,
+                                const int32_t* page_table, int32_t max_pages, const int32_t* lens,
+                                void* out, int32_t* err_flag, void* stream);
 
 /*
  * Causal paged attention of n_q consecutive queries of one sequence (the

@@ -251,3 +251,33 @@ def test_model_state_errors_without_gpu():
         assert e.value.status == 3
     finally:
         nq.nq_model_destroy(m)
+
+
+def test_static_attention_refuses_beyond_its_scratch_without_gpu():
+    """nq_attn_decode_static checks the split partials against its fixed
+    library scratch (NQ_ATTN_SCRATCH_BYTES) before it looks up or touches any
+    device memory: a batch and table width whose partials need more is
+    refused with NQ_ERR_OUT_OF_RANGE, as are shapes beyond the kernels. The
+    pointers are never dereferenced on these paths."""
+    import synth
+    cfg = nq.NQConfig.from_shape(synth.QWEN7B, 8, 32768)
+    fake = 1 << 20                                   # 16-byte aligned, never used
+    num_pages = 4096
+    kv = nq.nq_kv_alloc(cfg, fake, nq.nq_kv_pool_bytes(cfg, num_pages), num_pages)
+    try:
+        assert nq.NQ_ATTN_SCRATCH_BYTES == 24 << 20
+        assert nq.nq_attn_workspace_bytes(cfg, 8, 2048) <= nq.NQ_ATTN_SCRATCH_BYTES      # batch 8, 192 splits fit
+        for batch, pages in ((16, 2048), (64, 512), (64, 32768)):
+            need = nq.nq_attn_workspace_bytes(cfg, batch, pages)
+            assert need == 0 or need > nq.NQ_ATTN_SCRATCH_BYTES
+            with pytest.raises(nq.NQError) as e:
+                nq.nq_attn_decode_static(kv, 0, batch, fake, fake, pages, fake, fake, stream=0)
+            assert e.value.status == 3, (batch, pages)
+        with pytest.raises(nq.NQError) as e:             # argument checks as for nq_attn_decode
+            nq.nq_attn_decode_static(kv, 0, 1, fake + 8, fake, 4, fake, fake, stream=0)
+        assert e.value.status == 1
+        with pytest.raises(nq.NQError) as e:
+            nq.nq_attn_decode_static(kv, 28, 1, fake, fake, 4, fake, fake, stream=0)
+        assert e.value.status == 3
+    finally:
+        nq.nq_kv_free(kv)

@@ -22,7 +22,7 @@ __all__ = [
     "nq_status_str", "nq_last_error", "nq_layout_version", "nq_packed_size", "nq_pack_weights",
     "nq_unpack_weights", "nq_unpack_weights_dev", "nq_gemv_w4a16", "nq_config_check",
     "nq_kv_pool_bytes", "nq_kv_alloc", "nq_kv_append", "nq_kv_free", "nq_attn_workspace_bytes",
-    "nq_attn_decode", "nq_model_create", "nq_model_bind_layer", "nq_model_bind_head",
+    "nq_attn_decode", "nq_attn_decode_static", "NQ_ATTN_SCRATCH_BYTES", "nq_model_create", "nq_model_bind_layer", "nq_model_bind_head",
     "nq_rope_table_bytes", "nq_rope_table_fill", "nq_model_bind_rope", "nq_workspace_bytes",
     "nq_model_bind_workspace", "nq_model_destroy", "nq_decode_step", "nq_graph_capture",
     "nq_graph_launch", "nq_graph_kernel_count", "nq_graph_destroy", "nq_check_device_error",
@@ -114,6 +114,7 @@ _SIGS = {
     "nq_kv_free": (None, [_P]),
     "nq_attn_workspace_bytes": (_S, [_CFG, _I, _I]),
     "nq_attn_decode": (_I, [_P, _I, _I, _P, _P, _I, _P, _P, _P, _S, _P, _P]),
+    "nq_attn_decode_static": (_I, [_P, _I, _I, _P, _P, _I, _P, _P, _P, _P]),
     "nq_model_create": (_I, [_CFG, ctypes.POINTER(_P)]),
     "nq_model_bind_layer": (_I, [_P, _I, ctypes.POINTER(NQLayerPtrs)]),
     "nq_model_bind_head": (_I, [_P, _P, _P, _P]),
@@ -303,6 +304,14 @@ def nq_attn_decode(kv, layer, batch, q, page_table, max_pages, lens, out, worksp
                    stream=None):
     _check(lib().nq_attn_decode(kv, layer, batch, _ptr(q), _ptr(page_table), max_pages, _ptr(lens), _ptr(out),
                                 _ptr(workspace), ws_bytes, _ptr(err_flag), _stream(stream)), "nq_attn_decode")
+
+
+NQ_ATTN_SCRATCH_BYTES = 24 << 20
+
+
+def nq_attn_decode_static(kv, layer, batch, q, page_table, max_pages, lens, out, err_flag=None, stream=None):
+    _check(lib().nq_attn_decode_static(kv, layer, batch, _ptr(q), _ptr(page_table), max_pages, _ptr(lens), _ptr(out),
+                                       _ptr(err_flag), _stream(stream)), "nq_attn_decode_static")
 
 
 def nq_attn_prefill(kv, layer, n_q, start_pos, q, page_table, max_pages, out, err_flag=None, stream=None):

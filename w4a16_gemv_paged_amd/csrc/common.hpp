@@ -119,6 +119,12 @@ constexpr int32_t kAttnMaxPages = 32768;
 size_t attn_partial_bytes(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t splits);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
+// Library-owned device scratch (scratch.hip) of the entry points that allocate
+// nothing: kAttnScratchBytes per GPU; static_scratch gives the current device's
+// address (looked up once per device).
+constexpr size_t kAttnScratchBytes = NQ_ATTN_SCRATCH_BYTES;
+hipError_t static_scratch(void** out);
+
 hipError_t launch_kv_append(void* k_pool, void* v_pool, int32_t batch, int32_t n_kv,
                             int32_t head_dim, const int32_t* page_table, int32_t max_pages,
                             int32_t num_pages, const int32_t* pos, const void* k, const void* v,

@@ -586,19 +586,28 @@ size_t nq_attn_workspace_bytes(const nq_config* cfg, int32_t batch, int32_t max_
          align256(static_cast<size_t>(batch) * cfg->n_heads * S * 2 * 4);
 }
 
-nq_status nq_attn_decode(const nq_kv* kv, int32_t layer, int32_t batch, const void* q, const int32_t* page_table,
-                         int32_t max_pages, const int32_t* lens, void* out, void* workspace, size_t ws_bytes,
-                         int32_t* err_flag, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by nq_attn_decode and nq_attn_decode_static (the
+// workspace is checked by each caller).
+nq_status check_attn_args(const nq_kv* kv, int32_t layer, int32_t batch, const void* q, const int32_t* page_table,
+                          int32_t max_pages, const int32_t* lens, const void* out) {
   if (!kv) return fail(NQ_ERR_INVALID_ARG, "null kv");
   if (layer < 0 || layer >= kv->cfg.layers) return fail(NQ_ERR_OUT_OF_RANGE, "layer %d out of range", layer);
   if (batch < 1) return fail(NQ_ERR_INVALID_ARG, "batch must be >= 1");
   if (max_pages < 1) return fail(NQ_ERR_INVALID_ARG, "max_pages must be >= 1");
   if (max_pages > kAttnMaxPages) return fail(NQ_ERR_OUT_OF_RANGE, "max_pages %d > %d", max_pages, kAttnMaxPages);
-  if (!q || !page_table || !lens || !out || !workspace)
-    return fail(NQ_ERR_INVALID_ARG, "null pointer");
-  if (!aligned16(q) || !aligned16(workspace)) return fail(NQ_ERR_INVALID_ARG, "q and workspace must be 16-byte aligned");
-  if (ws_bytes < nq_attn_workspace_bytes(&kv->cfg, batch, max_pages))
-    return fail(NQ_ERR_INVALID_ARG, "attention workspace too small");
+  if (!q || !page_table || !lens || !out) return fail(NQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(q)) return fail(NQ_ERR_INVALID_ARG, "q must be 16-byte aligned");
+  return NQ_OK;
+}
+
+// Enqueues the attention of a checked call with its partials in ``workspace``.
+nq_status enqueue_attn(const nq_kv* kv, int32_t layer, int32_t batch, const void* q, const int32_t* page_table,
+                       int32_t max_pages, const int32_t* lens, void* out, void* workspace, int32_t* err_flag,
+                       void* stream) {
   const size_t lp = layer_pool_elems(kv->cfg, kv->num_pages);
   const uint16_t* kb = static_cast<const uint16_t*>(kv->pool) + static_cast<size_t>(layer) * 2 * lp;
   AttnArgs a{};
@@ -628,6 +637,39 @@ nq_status nq_attn_decode(const nq_kv* kv, int32_t layer, int32_t batch, const vo
   hipError_t e = launch_attention(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return NQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nq_status nq_attn_decode(const nq_kv* kv, int32_t layer, int32_t batch, const void* q, const int32_t* page_table,
+                         int32_t max_pages, const int32_t* lens, void* out, void* workspace, size_t ws_bytes,
+                         int32_t* err_flag, void* stream) {
+  nq_status st = check_attn_args(kv, layer, batch, q, page_table, max_pages, lens, out);
+  if (st != NQ_OK) return st;
+  if (!workspace) return fail(NQ_ERR_INVALID_ARG, "null workspace");
+  if (!aligned16(workspace)) return fail(NQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (ws_bytes < nq_attn_workspace_bytes(&kv->cfg, batch, max_pages))
+    return fail(NQ_ERR_INVALID_ARG, "attention workspace too small");
+  return enqueue_attn(kv, layer, batch, q, page_table, max_pages, lens, out, workspace, err_flag, stream);
+}
+
+nq_status nq_attn_decode_static(const nq_kv* kv, int32_t layer, int32_t batch, const void* q,
+                                const int32_t* page_table, int32_t max_pages, const int32_t* lens, void* out,
+                                int32_t* err_flag, void* stream) {
+  nq_status st = check_attn_args(kv, layer, batch, q, page_table, max_pages, lens, out);
+  if (st != NQ_OK) return st;
+  const size_t need = nq_attn_workspace_bytes(&kv->cfg, batch, max_pages);
+  if (need == 0)
+    return fail(NQ_ERR_OUT_OF_RANGE, "batch %d x max_pages %d is beyond the attention kernels", batch, max_pages);
+  if (need > kAttnScratchBytes)
+    return fail(NQ_ERR_OUT_OF_RANGE, "batch %d x max_pages %d needs %zu bytes of split partials, more than the "
+                "%zu-byte library scratch", batch, max_pages, need, kAttnScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = static_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "attention scratch lookup");
+  return enqueue_attn(kv, layer, batch, q, page_table, max_pages, lens, out, ws, err_flag, stream);
 }
 
 nq_status nq_attn_prefill(const nq_kv* kv, int32_t layer, int32_t n_q, int32_t start_pos, const void* q,

@@ -467,7 +467,8 @@ typedef struct nq_step_io {
   int32_t hist_len;
   int32_t* err_flag;        /* optional device int32: device-side range errors OR bits in
                                (1 = KV write, 2 = attention read, 4 = token id, 8 = NaN
-                               logits); NULL uses a flag inside the workspace              */
+                               logits, 16 = the persistent step's workgroups could not
+                               all run at once); NULL uses a flag inside the workspace     */
 } nq_step_io;
 
 /*
@@ -484,6 +485,33 @@ typedef struct nq_step_io {
  * bad io; NQ_ERR_HIP on launch failure.
  */
 nq_status nq_decode_step(nq_model* m, nq_kv* kv, const nq_step_io* io, void* stream);
+
+/*
+ * How a step is launched. NQ_STEP_AUTO (the default): at batch 1 the whole
+ * step is one persistent kernel when the device and model allow it (an
+ * MI355X's 256 CUs, head_dim 128 with 7 query heads per KV head or head_dim
+ * 64 with 4, at most 32 layers, at most 14 KV heads, max_pages <= 256 *
+ * min(64, 256 / n_kv_heads) (16384 for 4 KV heads), n_heads * head_dim ==
+ * hidden); other batches, and batch 1 otherwise, take the kernels listed
+ * above. NQ_STEP_KERNELS: always those kernels. Both compute the same
+ * operation (the persistent kernel splits the reductions differently, so the
+ * two agree within rounding, not bitwise).
+ *
+ * The persistent kernel runs 256 co-resident workgroups, one per CU, that
+ * hand each stage's output to the next through flags in the workspace; the
+ * workspace must be zeroed before its first step (a fresh hipMemset is
+ * enough) and must not be shared by steps that may run at the same time.
+ * Every wait inside it is bounded: if the workgroups cannot all be resident
+ * (another kernel occupying CUs), the step ends with err_flag bit 16 and
+ * garbage results, and the workspace must be zeroed again before the next
+ * step.
+ */
+enum { NQ_STEP_AUTO = 0, NQ_STEP_KERNELS = 1 };
+nq_status nq_model_set_step_mode(nq_model* m, int32_t mode);
+
+/* Kernels one step of this model launches at this batch and table width (1
+ * for the persistent kernel), or -1 for invalid arguments. Host only. */
+int32_t nq_step_kernels(const nq_model* m, int32_t batch, int32_t max_pages);
 
 /* ---------------------------------------------------------- chunked prefill */
 

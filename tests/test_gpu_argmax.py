@@ -97,16 +97,18 @@ def _scale_offset(shape, row, group):
 
 
 @pytest.mark.parametrize("shape", [SMALL, BIG], ids=["per-tile-head", "streaming-head"])
-def test_nan_logit_is_reported_and_the_step_completes(shape):
+@pytest.mark.parametrize("batch", [1, 2])
+def test_nan_logit_is_reported_and_the_step_completes(shape, batch):
+    """At batch 1 the step is the persistent kernel, at batch 2 the kernel per stage."""
     dm = _model(shape, synth.head_params(shape, seed=0))
     off = _scale_offset(shape, 123, 0)
     saved = dm.lm[off:off + 2].clone()
     dm.lm[off:off + 2] = torch.tensor([0x00, 0x7E], dtype=torch.uint8, device="cuda")   # fp16 NaN
-    prompts = [synth.prompt_ids(3, shape.vocab, seed=85 + b) for b in range(2)]
-    pt, total = synth.decode_page_tables(2, 4, seed=3, spare_pages=2)
+    prompts = [synth.prompt_ids(3, shape.vocab, seed=85 + b) for b in range(batch)]
+    pt, total = synth.decode_page_tables(batch, 4, seed=3, spare_pages=2)
     kv = KVCache(dm, total, poison=True)
     st = Stepper(dm, kv, pt, want_logits=True)
-    st.set_pos(np.zeros(2, np.int32))
+    st.set_pos(np.zeros(batch, np.int32))
     st.set_tokens([p[0] for p in prompts])
     say("NaN logit step", shape.name)
     st.step()
@@ -125,7 +127,7 @@ def test_nan_logit_is_reported_and_the_step_completes(shape):
     st.check()
     z = st.logits.cpu().numpy()
     assert np.all(np.isfinite(z))
-    np.testing.assert_array_equal(st.tokens.cpu().numpy(), [oracle.argmax_lowest(z[b]) for b in range(2)])
+    np.testing.assert_array_equal(st.tokens.cpu().numpy(), [oracle.argmax_lowest(z[b]) for b in range(batch)])
     st.close()
     kv.close()
     dm.close()

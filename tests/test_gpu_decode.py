@@ -1,7 +1,9 @@
 """End-to-end GPU decode parity against the oracle (tiny Qwen2-style config).
 
 Run: 16-token prompt, 32 greedy tokens, KV in 16-token pages ending on a
-partial page (47 cached positions = 2 full pages + 15)."""
+partial page (47 cached positions = 2 full pages + 15). Every test runs in both
+step modes: "auto" (batch 1 as the persistent whole-step kernel) and
+"kernels" (one kernel per stage)."""
 import numpy as np
 import pytest
 import torch
@@ -19,15 +21,26 @@ PROMPT_LEN, N_GEN = 16, 32
 TOL_LAYER, TOL_LOGITS, MARGIN = 2e-3, 5e-3, 1e-2
 
 
-@pytest.fixture(scope="module")
-def tiny():
+@pytest.fixture(scope="module", params=["auto", "kernels"])
+def tiny(request):
     layers = [synth.layer_params(SHAPE, i, seed=0) for i in range(SHAPE.layers)]
     head = synth.head_params(SHAPE, seed=0)
     om = OracleModel.build(SHAPE, layers, head)
-    say("build tiny device model")
+    say("build tiny device model, step mode", request.param)
     dm = DeviceModel(SHAPE, lambda i: layers[i], head, max_batch=8, max_pos=4096)
+    dm.set_step_mode(request.param)
+    dm.mode = request.param
     yield om, dm
     dm.close()
+
+
+def _expected_kernels(dm, batch, max_pages):
+    n = dm.step_kernels(batch, max_pages)
+    if dm.mode == "auto" and batch == 1:
+        assert n == 1           # the persistent step is what runs (MI355X, 256 CUs)
+    else:
+        assert n > 1
+    return n
 
 
 def _run(dm, prompts, n_gen, graph=False, pages=None, seed=3, layers=True):
@@ -46,6 +59,7 @@ def _run(dm, prompts, n_gen, graph=False, pages=None, seed=3, layers=True):
     out["page_table"] = pt
     out["hist"] = st.hist.cpu().numpy()
     out["kernels"] = None
+    out["max_pages"] = max_pages
     if graph:
         from w4a16_gemv_paged_amd import nq_graph_kernel_count
         out["kernels"] = nq_graph_kernel_count(st.graph)
@@ -148,7 +162,7 @@ def test_graph_replay_equals_eager_bitwise(tiny, tiny_run):
     np.testing.assert_array_equal(g["tokens"], eager["tokens"])
     np.testing.assert_array_equal(g["logits"].view(np.uint32), eager["logits"].view(np.uint32))
     np.testing.assert_array_equal(g["layer_out"].view(np.uint16), eager["layer_out"].view(np.uint16))
-    assert g["kernels"] in (5 * SHAPE.layers + 2, 6 * SHAPE.layers + 2)   # attention combine only when split
+    assert g["kernels"] == _expected_kernels(dm, 1, g["max_pages"])
 
 
 def test_batched_ragged_equals_single_sequences(tiny):
@@ -178,11 +192,12 @@ def test_batch8_logits_against_oracle(tiny):
 
 
 def test_split_attention_long_context(tiny):
-    """Batch 1 over 64-page tables: attention splits the pages over 16
-    workgroups per KV head (4 pages each, one per wave) whose partials the
-    combine kernel merges. 200-token prompt (13-14 pages in use: four splits
-    hold pages, the rest are empty). Logits and tokens against the oracle;
-    graph replay equals eager bitwise."""
+    """Batch 1 over 64-page tables, 200-token prompt (13-14 pages in use). One
+    kernel per stage: the pages split over 16 workgroups per KV head (4 pages
+    each, one per wave; four splits hold pages, the rest are empty) whose
+    partials the combine kernel merges. Persistent step: one split of all the
+    pages per KV head. Logits and tokens against the oracle; graph replay
+    equals eager bitwise."""
     om, dm = tiny
     prompt = synth.prompt_ids(200, SHAPE.vocab, seed=60)
     say("tiny long-context eager run")
@@ -196,7 +211,25 @@ def test_split_attention_long_context(tiny):
     say("tiny long-context graph run")
     g = _run(dm, [prompt], 8, pages=64, graph=True, layers=False)
     np.testing.assert_array_equal(g["logits"].view(np.uint32), gpu["logits"].view(np.uint32))
-    assert g["kernels"] == 6 * SHAPE.layers + 2
+    assert g["kernels"] == _expected_kernels(dm, 1, 64)
+
+
+def test_split_attention_many_splits(tiny):
+    """Batch 1 at a 2500-token context (157 pages): the persistent step splits
+    each KV head's pages four ways (40 pages per workgroup, 10 per attention
+    wave), and the last split to finish merges the four in LDS in two chunks
+    (three splits' partials fit its staging area at this shape). Logits and
+    tokens against the oracle."""
+    om, dm = tiny
+    prompt = synth.prompt_ids(2500, SHAPE.vocab, seed=61)
+    say("tiny 2500-token context run")
+    gpu = _run(dm, [prompt], 4, layers=False)
+    orc = oracle.generate(om, prompt, 4, forced=gpu["tokens"][0])
+    gl = gpu["logits"][len(prompt) - 1:, 0]
+    errs = [rel_inf(gl[i], orc["logits"][i]) for i in range(4)]
+    assert max(errs) < TOL_LOGITS, max(errs)
+    ok = orc["margins"] > MARGIN
+    np.testing.assert_array_equal(gpu["tokens"][0][ok], orc["tokens"][ok])
 
 
 def test_split_attention_batch8(tiny):
@@ -215,7 +248,7 @@ def test_split_attention_batch8(tiny):
         np.testing.assert_array_equal(gpu["tokens"][b][ok], orc["tokens"][ok])
     say("tiny long-context batch-8 graph run")
     g = _run(dm, prompts, 3, pages=64, graph=True, layers=False)
-    assert g["kernels"] == 6 * SHAPE.layers + 2
+    assert g["kernels"] == _expected_kernels(dm, 8, 64) == 6 * SHAPE.layers + 2
     np.testing.assert_array_equal(g["logits"].view(np.uint32), gpu["logits"].view(np.uint32))
 
 
@@ -227,6 +260,7 @@ def test_model_from_container_decodes_identically(tiny, tmp_path):
     write_container(path, SHAPE, lambda l: synth.layer_params(SHAPE, l, seed=0), synth.head_params(SHAPE, seed=0))
     say("tiny model from container")
     dm2 = DeviceModel.load(path, max_batch=8, max_pos=4096)
+    dm2.set_step_mode(dm.mode)
     prompt = synth.prompt_ids(PROMPT_LEN, SHAPE.vocab, seed=2)
     a = _run(dm, [prompt], 8, layers=False)
     b = _run(dm2, [prompt], 8, layers=False)

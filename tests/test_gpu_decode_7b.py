@@ -37,11 +37,15 @@ LAYERS = (0, 13, 27)
 TOL_LAYER, TOL_LOGITS, MARGIN = 2e-3, 5e-3, 1e-2
 
 
-@pytest.fixture(scope="module")
-def model7b():
-    say("build 7B device model")
+@pytest.fixture(scope="module", params=["auto", "kernels"])
+def model7b(request):
+    """The 7B-shaped model in each step mode: "auto" runs batch 1 as the
+    persistent whole-step kernel, "kernels" one kernel per stage."""
+    say("build 7B device model, step mode", request.param)
     head = synth.head_params(SHAPE, seed=0)
     dm = DeviceModel(SHAPE, lambda l: synth.layer_params(SHAPE, l, seed=0), head, max_batch=8, max_pos=4096)
+    dm.set_step_mode(request.param)
+    assert dm.step_kernels(1, 52) == (1 if request.param == "auto" else 6 * SHAPE.layers + 2)
     yield dm, head
     dm.close()
     del dm

@@ -22,7 +22,8 @@ __all__ = [
     "nq_status_str", "nq_last_error", "nq_layout_version", "nq_packed_size", "nq_pack_weights",
     "nq_unpack_weights", "nq_unpack_weights_dev", "nq_gemv_w4a16", "nq_config_check",
     "nq_kv_pool_bytes", "nq_kv_alloc", "nq_kv_append", "nq_kv_free", "nq_attn_workspace_bytes",
-    "nq_attn_decode", "nq_attn_decode_static", "NQ_ATTN_SCRATCH_BYTES", "nq_model_create", "nq_model_bind_layer", "nq_model_bind_head",
+    "nq_attn_decode", "nq_attn_decode_static", "NQ_ATTN_SCRATCH_BYTES", "nq_model_create",
+    "nq_model_set_step_mode", "nq_step_kernels", "NQ_STEP_AUTO", "NQ_STEP_KERNELS", "nq_model_bind_layer", "nq_model_bind_head",
     "nq_rope_table_bytes", "nq_rope_table_fill", "nq_model_bind_rope", "nq_workspace_bytes",
     "nq_model_bind_workspace", "nq_model_destroy", "nq_decode_step", "nq_graph_capture",
     "nq_graph_launch", "nq_graph_kernel_count", "nq_graph_destroy", "nq_check_device_error",
@@ -124,6 +125,8 @@ _SIGS = {
     "nq_workspace_bytes": (_S, [_CFG, _I, _I]),
     "nq_model_bind_workspace": (_I, [_P, _P, _S]),
     "nq_model_destroy": (None, [_P]),
+    "nq_model_set_step_mode": (_I, [_P, _I]),
+    "nq_step_kernels": (_I, [_P, _I, _I]),
     "nq_decode_step": (_I, [_P, _P, ctypes.POINTER(NQStepIO), _P]),
     "nq_graph_capture": (_I, [_P, _P, ctypes.POINTER(NQStepIO), _P, ctypes.POINTER(_P)]),
     "nq_graph_launch": (_I, [_P, _P]),
@@ -320,6 +323,17 @@ def nq_attn_prefill(kv, layer, n_q, start_pos, q, page_table, max_pages, out, er
 
 
 # ------------------------------------------------------------------ model, step, graph
+
+NQ_STEP_AUTO, NQ_STEP_KERNELS = 0, 1
+
+
+def nq_model_set_step_mode(model, mode: int) -> None:
+    _check(lib().nq_model_set_step_mode(model, mode), "nq_model_set_step_mode")
+
+
+def nq_step_kernels(model, batch: int, max_pages: int) -> int:
+    return lib().nq_step_kernels(model, batch, max_pages)
+
 
 def nq_model_create(cfg: NQConfig) -> int:
     h = _P()

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnq.so")
 
-SOURCES = ["host_pack.cpp", "runtime.cpp", "container.cpp", "kernels.hip", "prefill.hip", "w4a8.hip", "scratch.hip"]
+SOURCES = ["host_pack.cpp", "runtime.cpp", "container.cpp", "kernels.hip", "prefill.hip", "w4a8.hip", "scratch.hip", "step.hip"]
 ARCH = "gfx950"
 
 # Device code must not use packed-FP32 instructions (v_pk_*_f32); the feature

@@ -136,6 +136,72 @@ hipError_t launch_argmax_finalize(const float* vals, const int32_t* idx, int32_t
                                   int32_t* tokens, int32_t* pos, int32_t* hist, int32_t hist_len, int32_t pos_set,
                                   hipStream_t s);
 
+// ------------------------------------------------------------ persistent batch-1 step
+
+// The whole batch-1 decode step as one launch of kPsWG co-resident
+// workgroups (step.hip): one per CU of an MI355X, kPsXcds XCDs of 32 CUs.
+constexpr int kPsWG = 256;
+constexpr int kPsXcds = 8;
+constexpr int kPsMaxSplits = 64;    // attention splits per KV head (at most 14 KV heads)
+constexpr int kPsMaxLayers = 32;    // per-layer pointers travel in the kernel arguments
+constexpr int kPsMaxPages = 16384;  // page-table width (64 splits of 4 waves x 64 pages)
+constexpr int kPsSegGroups = 4;     // groups per fixed summation segment of a tile
+
+struct PsLayer {
+  const uint8_t* qkv;
+  const uint16_t* bias;   // fp16
+  const uint8_t* o;
+  const uint8_t* gu;
+  const uint8_t* d;
+  const uint16_t* g1;     // fp16 gains
+  const uint16_t* g2;
+};
+
+struct PsParams {
+  PsLayer layer[kPsMaxLayers];
+  int L, H, I, nh, nkv, hd, V;
+  int kmax, maxu;                   // longest staged row; most (tile, segment) units per workgroup
+  int sc_a, sc_b;                   // LDS bytes of the scale buffers (QKV / gate-up / LM; O / down)
+  const uint16_t* embed;
+  const uint16_t* gfinal;
+  const uint8_t* lm;
+  const float* rope;
+  int max_pos;
+  uint16_t* kpool;                  // K pool of layer 0; V of layer l at + (2l + 1) * layer_pool
+  size_t layer_pool;                // fp16 elements of one layer's K (or V) pages
+  int num_pages;
+  const int32_t* pt;                // the sequence's page-table row
+  int max_pages;
+  int32_t* tokens;
+  int32_t* pos;
+  int32_t* hist;
+  int hist_len;
+  float* logits;                    // optional [V]
+  uint16_t* layer_out;              // optional [L][H]
+  int32_t* err;
+  float eps;
+  // workspace: hand-off flags, counters and buffers
+  int* xflag;                       // [8][64] per-workgroup epochs, one row per XCD
+  int* xcdflag;                     // [8][16] per-XCD epochs
+  int* cnt;                         // [16][16] split counters per KV head; row 14: per-XCD slot
+                                    // tickets; row 15: LM head
+  int* abort;
+  uint16_t* hbuf;                   // [H] residual stream
+  uint16_t* qbuf;                   // [nh * hd] q after RoPE
+  uint16_t* ao;                     // [nh * hd] attention output
+  uint16_t* act;                    // [I] SwiGLU output
+  float* apart;                     // [nkv][kPsMaxSplits][nh / nkv][hd + 4] split partials: output, max, sum, pad
+  float* lmval;                     // [kPsWG] greedy partials
+  int32_t* lmidx;
+  int max_polls;                    // bound of every wait
+};
+size_t ps_lds_bytes(const PsParams& p);
+bool ps_supported(int head_dim, int n_heads, int n_kv);
+hipError_t launch_decode_step_persistent(const PsParams& p, hipStream_t s);
+// The current device can hold the persistent step: kPsWG CUs, one workgroup
+// of the kernel resident on each (checked once per device).
+bool ps_device_ok();
+
 // ------------------------------------------------------------ chunked prefill
 
 constexpr int32_t kPrefillMaxChunk = 4096;  // rows of one prefill GEMM / attention call

@@ -151,6 +151,7 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) { retur
 // for LDS/scalar memory and until at most n vector-memory operations are
 // outstanding.
 constexpr int kWaitLgkm0 = 0xC07F;
+constexpr int kWaitVm0 = 0x0F70;    // s_waitcnt vmcnt(0) alone
 constexpr int wait_vm_lgkm0(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
 
 }  // namespace nq

@@ -23,6 +23,7 @@ struct nq_model {
   const float* rope = nullptr;
   void* ws = nullptr;
   size_t ws_bytes = 0;
+  int32_t step_mode = NQ_STEP_AUTO;
 };
 
 struct nq_kv {
@@ -43,6 +44,20 @@ namespace {
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct Workspace {
+  // the persistent step's hand-off state and buffers: first, at offsets that
+  // do not depend on the batch or table width, so that the epoch flags a
+  // workgroup left at the end of one step are where the next step looks
+  int* xflag;
+  int* xcdflag;
+  int* cnt;
+  int* abort;
+  void* ps_h;
+  void* ps_q;
+  void* ps_ao;
+  void* ps_act;
+  float* apart;
+  float* lmval;
+  int32_t* lmidx;
   int32_t* err;
   void* h;
   void* qbuf;
@@ -65,6 +80,18 @@ Workspace carve(const nq_config& c, int32_t batch, int32_t max_pages, uint8_t* b
     return p;
   };
   const int32_t qd = c.n_heads * c.head_dim;
+  w.xflag = reinterpret_cast<int*>(take(static_cast<size_t>(kPsXcds) * 64 * 4));
+  w.xcdflag = reinterpret_cast<int*>(take(static_cast<size_t>(kPsXcds) * 16 * 4));
+  w.cnt = reinterpret_cast<int*>(take(16 * 16 * 4));
+  w.abort = reinterpret_cast<int*>(take(256));
+  w.ps_h = take(static_cast<size_t>(c.hidden) * 2);
+  w.ps_q = take(static_cast<size_t>(qd) * 2);
+  w.ps_ao = take(static_cast<size_t>(qd) * 2);
+  w.ps_act = take(static_cast<size_t>(c.intermediate) * 2);
+  w.apart = reinterpret_cast<float*>(take(static_cast<size_t>(c.n_kv_heads) * kPsMaxSplits *
+                                          (c.n_heads / c.n_kv_heads) * (c.head_dim + 4) * 4));
+  w.lmval = reinterpret_cast<float*>(take(kPsWG * 4));
+  w.lmidx = reinterpret_cast<int32_t*>(take(kPsWG * 4));
   w.attn = attn_plan(batch, c.n_kv_heads, max_pages);
   w.err = reinterpret_cast<int32_t*>(take(256));
   w.h = take(static_cast<size_t>(batch) * c.hidden * 2);
@@ -115,8 +142,92 @@ nq_status check_model_ready(const nq_model* m, const nq_kv* kv, const nq_step_io
   return NQ_OK;
 }
 
+// Whether a step of this model and io runs as the persistent batch-1 kernel.
+bool use_persistent(const nq_model* m, const nq_step_io* io) {
+  const nq_config& c = m->cfg;
+  if (m->step_mode != NQ_STEP_AUTO || io->batch != 1) return false;
+  if (c.layers > kPsMaxLayers || io->max_pages > kPsMaxPages) return false;
+  // a split holds at most 64 pages per attention wave, and every split its workgroup
+  if (c.n_kv_heads < 1 || io->max_pages > 256 * std::min(kPsMaxSplits, kPsWG / c.n_kv_heads)) return false;
+  if (!ps_supported(c.head_dim, c.n_heads, c.n_kv_heads) || c.n_kv_heads > 14) return false;
+  // at most 8 QKV tiles and one O / down tile per workgroup (the control
+  // wave's epilogue lanes)
+  const int64_t t_qkv = tiles_of((c.n_heads + 2 * c.n_kv_heads) * c.head_dim), t_h = tiles_of(c.hidden);
+  if (t_qkv > 8 * kPsWG || t_h > kPsWG || c.n_heads * c.head_dim != c.hidden) return false;
+  return ps_device_ok();
+}
+
+int enqueue_step_persistent(nq_model* m, nq_kv* kv, const nq_step_io* io, hipStream_t s) {
+  const nq_config& c = m->cfg;
+  Workspace w = carve(c, 1, io->max_pages, static_cast<uint8_t*>(m->ws));
+  PsParams p{};
+  for (int l = 0; l < c.layers; ++l) {
+    const nq_layer_ptrs& L = m->layers[l];
+    p.layer[l] = PsLayer{static_cast<const uint8_t*>(L.qkv_packed), static_cast<const uint16_t*>(L.qkv_bias),
+                         static_cast<const uint8_t*>(L.o_packed), static_cast<const uint8_t*>(L.gate_up_packed),
+                         static_cast<const uint8_t*>(L.down_packed), static_cast<const uint16_t*>(L.attn_norm),
+                         static_cast<const uint16_t*>(L.mlp_norm)};
+  }
+  p.L = c.layers;
+  p.H = c.hidden;
+  p.I = c.intermediate;
+  p.nh = c.n_heads;
+  p.nkv = c.n_kv_heads;
+  p.hd = c.head_dim;
+  p.V = c.vocab;
+  p.kmax = std::max(c.hidden, c.intermediate);
+  // most (tile, segment) units of one matrix per workgroup
+  const int64_t qkv_rows = static_cast<int64_t>(c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const int64_t shapes[5][2] = {{qkv_rows, c.hidden}, {c.hidden, c.hidden}, {2LL * c.intermediate, c.hidden},
+                                {c.hidden, c.intermediate}, {c.vocab, c.hidden}};
+  int64_t maxu = 1, sc[5] = {};
+  for (int k = 0; k < 5; ++k) {
+    const int64_t tiles = (tiles_of(static_cast<int32_t>(shapes[k][0])) + kPsWG - 1) / kPsWG;
+    const int64_t segs = (shapes[k][1] / kGroup + kPsSegGroups - 1) / kPsSegGroups;
+    maxu = std::max(maxu, tiles * segs);
+    sc[k] = tiles * (shapes[k][1] / kGroup) * 32;  // a workgroup's group scales
+  }
+  p.maxu = static_cast<int>(maxu);
+  p.sc_a = static_cast<int>(std::max({sc[0], sc[2], sc[4]}));
+  p.sc_b = static_cast<int>(std::max(sc[1], sc[3]));
+  p.embed = static_cast<const uint16_t*>(m->embed);
+  p.gfinal = static_cast<const uint16_t*>(m->final_norm);
+  p.lm = static_cast<const uint8_t*>(m->lm);
+  p.rope = m->rope;
+  p.max_pos = c.max_pos;
+  p.kpool = static_cast<uint16_t*>(kv->pool);
+  p.layer_pool = layer_pool_elems(c, kv->num_pages);
+  p.num_pages = kv->num_pages;
+  p.pt = io->page_table;
+  p.max_pages = io->max_pages;
+  p.tokens = io->tokens;
+  p.pos = io->pos;
+  p.hist = io->token_hist;
+  p.hist_len = io->hist_len;
+  p.logits = io->logits;
+  p.layer_out = static_cast<uint16_t*>(io->layer_out);
+  p.err = io->err_flag ? io->err_flag : w.err;
+  p.eps = c.rms_eps;
+  p.xflag = w.xflag;
+  p.xcdflag = w.xcdflag;
+  p.cnt = w.cnt;
+  p.abort = w.abort;
+  p.hbuf = static_cast<uint16_t*>(w.ps_h);
+  p.qbuf = static_cast<uint16_t*>(w.ps_q);
+  p.ao = static_cast<uint16_t*>(w.ps_ao);
+  p.act = static_cast<uint16_t*>(w.ps_act);
+  p.apart = w.apart;
+  p.lmval = w.lmval;
+  p.lmidx = w.lmidx;
+  p.max_polls = 1 << 20;
+  const hipError_t e = launch_decode_step_persistent(p, s);
+  if (e != hipSuccess) return hip_fail(e, "persistent step launch"), -1;
+  return 1;
+}
+
 // Enqueue one decode step. Returns the number of kernels launched (>= 0) or -1.
 int enqueue_step(nq_model* m, nq_kv* kv, const nq_step_io* io, hipStream_t s) {
+  if (use_persistent(m, io)) return enqueue_step_persistent(m, kv, io, s);
   const nq_config& c = m->cfg;
   const int B = io->batch;
   Workspace w = carve(c, B, io->max_pages, static_cast<uint8_t*>(m->ws));
@@ -761,6 +872,23 @@ nq_status nq_model_bind_workspace(nq_model* m, void* ws, size_t bytes) {
   m->ws = ws;
   m->ws_bytes = bytes;
   return NQ_OK;
+}
+
+nq_status nq_model_set_step_mode(nq_model* m, int32_t mode) {
+  if (!m) return fail(NQ_ERR_INVALID_ARG, "null model");
+  if (mode != NQ_STEP_AUTO && mode != NQ_STEP_KERNELS) return fail(NQ_ERR_INVALID_ARG, "unknown step mode %d", mode);
+  m->step_mode = mode;
+  return NQ_OK;
+}
+
+int32_t nq_step_kernels(const nq_model* m, int32_t batch, int32_t max_pages) {
+  if (!m || batch < 1) return -1;
+  nq_step_io io{};
+  io.batch = batch;
+  io.max_pages = max_pages;
+  if (use_persistent(m, &io)) return 1;
+  const AttnPlan a = attn_plan(batch, m->cfg.n_kv_heads, max_pages);
+  return m->cfg.layers * (a.S > 1 ? 6 : 5) + 2;
 }
 
 void nq_model_destroy(nq_model* m) { delete m; }

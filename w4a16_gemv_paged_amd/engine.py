@@ -21,7 +21,10 @@ from . import (NQConfig, NQLayerPtrs, NQStepIO, NQ_MAT_PLAIN, NQ_MAT_QKV, NQ_MAT
                nq_rope_table_fill, nq_workspace_bytes, nq_model_bind_workspace, nq_model_destroy,
                nq_kv_pool_bytes, nq_kv_alloc, nq_kv_free, nq_decode_step, nq_graph_capture, nq_graph_launch,
                nq_graph_destroy, nq_graph_kernel_count, nq_check_device_error, NQPrefillIO,
-               nq_prefill_workspace_bytes, nq_prefill)
+               nq_prefill_workspace_bytes, nq_prefill, nq_model_set_step_mode, nq_step_kernels, NQ_STEP_AUTO,
+               NQ_STEP_KERNELS)
+
+STEP_MODES = {"auto": NQ_STEP_AUTO, "kernels": NQ_STEP_KERNELS}
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -126,6 +129,14 @@ class DeviceModel:
         nq_model_bind_head(self.handle, self.embed, self.g_final, self.lm)
         self.rope = to_device(nq_rope_table_fill(self.cfg), self.device)
         nq_model_bind_rope(self.handle, self.rope)
+
+    def set_step_mode(self, mode: str) -> None:
+        """"auto": the persistent whole-step kernel at batch 1 where supported;
+        "kernels": the kernel-per-stage step at every batch."""
+        nq_model_set_step_mode(self.handle, STEP_MODES[mode])
+
+    def step_kernels(self, batch: int, max_pages: int) -> int:
+        return nq_step_kernels(self.handle, batch, max_pages)
 
     def weight_bytes(self) -> int:
         n = sum(t.numel() * t.element_size() for t in self._keep)

@@ -42,10 +42,11 @@ constexpr int kPsCtrl = kPsStream;            // the control wave
 constexpr int kPsAttWave0 = kPsStream + 1;    // first attention wave
 constexpr int kPsAtt = 4;                     // attention waves
 constexpr int kPsWaves = kPsStream + 1 + kPsAtt;
-constexpr int kPsRing = 24;                   // weight blocks in flight per streaming wave
+constexpr int kPsSeg = kPsSegGroups;          // blocks (groups) per unit: a tile's summation segment
+constexpr int kPsRingUnits = 6;               // units in flight per streaming wave
+constexpr int kPsRing = kPsRingUnits * kPsSeg;  // weight blocks in flight per streaming wave
 constexpr int kPsPerXcd = kPsWG / kPsXcds;    // workgroups per XCD
 constexpr int kAbortBit = 16;
-constexpr int kPsSeg = kPsSegGroups;  // groups per summation segment
 
 __device__ __forceinline__ const half_t* hc(const uint16_t* x) { return reinterpret_cast<const half_t*>(x); }
 __device__ __forceinline__ half_t* hm(uint16_t* x) { return reinterpret_cast<half_t*>(x); }
@@ -96,15 +97,15 @@ __device__ __forceinline__ int ld_i_sc1(const int32_t* p) {
 // GEMV stage kinds in the step's sequence (per layer QKV, ATT, O, GU, D; then LM)
 enum PsKind : int { K_QKV = 0, K_ATT = 1, K_O = 2, K_GU = 3, K_D = 4, K_LM = 5 };
 
-// A tile's K is summed over fixed segments of kPsSeg groups, each computed
-// whole by one wave and added in segment order, so a row's result does not
-// depend on the tile or workgroup it falls in (rows with equal weights give
-// bitwise equal outputs). The waves split a workgroup's (tile, segment) units
-// evenly; a wave's units cover consecutive blocks.
+// A tile's K is summed over fixed segments of kPsSeg groups (units), each
+// computed whole by one wave and added in segment order, so a row's result
+// does not depend on the tile or workgroup it falls in (rows with equal
+// weights give bitwise equal outputs). The waves split a workgroup's (tile,
+// segment) units evenly; unit u is segment u % nseg of tile u / nseg.
 struct Geo {  // one GEMV stage for this workgroup and wave
   int T, G, t0, nt;     // tiles of the matrix, groups per tile, this workgroup's tiles [t0, t0+nt)
   int nseg;             // segments per tile
-  int wb0, wb1;         // this wave's blocks [wb0, wb1) of the workgroup's nt * G
+  int u0, u1;           // this wave's units [u0, u1) of the workgroup's nt * nseg
 };
 
 __device__ __forceinline__ Geo ps_geo(const PsParams& p, int kind, int wg, int wave) {
@@ -124,11 +125,8 @@ __device__ __forceinline__ Geo ps_geo(const PsParams& p, int kind, int wg, int w
   g.nt = static_cast<int>(static_cast<int64_t>(g.T) * (wg + 1) / kPsWG) - g.t0;
   g.nseg = (g.G + kPsSeg - 1) / kPsSeg;
   const int nu = g.nt * g.nseg;
-  const int u0 = nu * wave / kPsStream, u1 = nu * (wave + 1) / kPsStream;
-  // first block of unit u (u = nu gives the end)
-  const int t0u = u0 / g.nseg, t1u = u1 / g.nseg;
-  g.wb0 = t0u * g.G + min(g.G, (u0 - t0u * g.nseg) * kPsSeg);
-  g.wb1 = t1u * g.G + min(g.G, (u1 - t1u * g.nseg) * kPsSeg);
+  g.u0 = nu * wave / kPsStream;
+  g.u1 = nu * (wave + 1) / kPsStream;
   return g;
 }
 
@@ -240,23 +238,25 @@ __device__ __forceinline__ half_t ps_prescale(half_t v, int k) {
   return v * static_cast<half_t>(high_scale(k & 7));
 }
 
-// Control wave: xs = x * fp16(gain * pre-scale) in place (fp16 products), with
-// x staged in xs and the gain in gs; returns this lane's part of the sum of
-// squares of x (fp32).
+// Control wave: the staged row of K activations in xs taken times fp16(gain *
+// pre-scale) in place (fp16 products, as the GEMV would form them; the gain is
+// staged in gs). Returns this lane's part of the sum of squares of the row
+// before the gain (fp32 accumulation of exact fp16 products).
 __device__ __forceinline__ float ps_stage_gain(half_t* xs, const half_t* gs, int K) {
   const int lane = threadIdx.x & 63;
+  const h2 sixteenth = {static_cast<half_t>(0.0625f), static_cast<half_t>(0.0625f)};
   float ss = 0.0f;
   for (int i = lane; i < K / 8; i += 64) {
     uint4 v = *reinterpret_cast<const uint4*>(xs + i * 8);
-    const uint4 g = *reinterpret_cast<const uint4*>(gs + i * 8);
-    half_t* hv = reinterpret_cast<half_t*>(&v);
-    const half_t* hg = reinterpret_cast<const half_t*>(&g);
+    const uint4 gv = *reinterpret_cast<const uint4*>(gs + i * 8);
+    h2* x = reinterpret_cast<h2*>(&v);
+    const h2* g = reinterpret_cast<const h2*>(&gv);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float f = static_cast<float>(hv[e]);
-      ss = fmaf(f, f, ss);
-      hv[e] = hv[e] * static_cast<half_t>(static_cast<float>(hg[e]) * high_scale(e));
-    }
+    for (int q = 0; q < 4; ++q) ss = __builtin_amdgcn_fdot2(x[q], x[q], ss, false);
+    x[0] = x[0] * g[0];
+    x[1] = x[1] * (g[1] * sixteenth);
+    x[2] = x[2] * g[2];
+    x[3] = x[3] * (g[3] * sixteenth);
     *reinterpret_cast<uint4*>(xs + i * 8) = v;
   }
   return ss;
@@ -309,91 +309,105 @@ __device__ __forceinline__ void ps_streaming(const PsParams& p, const PsLds& s, 
   const half8 nbias = neg_bias_frag();
 
   // This wave's geometry of each GEMV kind (the same in every layer), once,
-  // into its LDS table: blocks, first block in the matrix, groups, segments.
+  // into its LDS table: units, first unit, groups per tile, segments per tile.
   int* geo = s.geo + wave * 6 * 4;
   if (lane < 6) {
     const Geo g = ps_geo(p, lane, wg, wave);
     const bool gemv = lane != K_ATT;
-    geo[lane * 4 + 0] = gemv ? g.wb1 - g.wb0 : 0;
-    geo[lane * 4 + 1] = gemv ? g.t0 * g.G + g.wb0 : 0;
+    geo[lane * 4 + 0] = gemv ? g.u1 - g.u0 : 0;
+    geo[lane * 4 + 1] = gemv ? g.u0 : 0;
     geo[lane * 4 + 2] = gemv ? g.G : 1;
     geo[lane * 4 + 3] = gemv ? g.nseg : 1;
   }
   wave_sync();
-  auto gcount = [&](int st) { return __builtin_amdgcn_readfirstlane(geo[ps_stage_kind(st, L) * 4]); };
-  // blocks of the whole sequence, processed in passes of kPsRing
-  const int per_layer = gcount(K_QKV) + gcount(K_O) + gcount(K_GU) + gcount(K_D);
-  const int total = L * per_layer + gcount(last);
-  const int passes = (total + kPsRing - 1) / kPsRing;
+  auto field = [&](int kind, int f) { return __builtin_amdgcn_readfirstlane(geo[kind * 4 + f]); };
+  auto units = [&](int st) { return field(ps_stage_kind(st, L), 0); };
+  // units of the whole sequence, processed in passes of kPsRingUnits
+  const int per_layer = units(K_QKV) + units(K_O) + units(K_GU) + units(K_D);
+  const int total = L * per_layer + units(last);
+  const int passes = (total + kPsRingUnits - 1) / kPsRingUnits;
 
-  // load cursor: stage, block within this wave's range, descriptor (a
-  // zero-length descriptor once the sequence is done: its loads return 0 and
-  // touch no memory, so every slot is refilled the same way)
-  int lst = 0, lj = 0, lcount = 0;
+  // Load cursor: stage, units requested, (tile, segment) of the next unit,
+  // and the descriptor of this workgroup's tiles of the stage's matrix. Once
+  // the sequence is requested the descriptor is zero-length: its loads return
+  // 0 and touch no memory, so every slot is refilled the same way. The blocks
+  // past a tile's last group (a short last segment) read the next tile's
+  // blocks, or zeros past the workgroup's tiles; their products are dropped.
+  int lst = 0, lk = 0, lnu = 0, lG = 1, lnseg = 1, ltl = 0, lseg = 0;
+  bool lend = false;
   __amdgpu_buffer_rsrc_t lw = rsrc(nullptr, 0);
   auto load_stage = [&](int st) {
     const int kind = ps_stage_kind(st, L);
-    lcount = gcount(st);
-    const size_t b0 = static_cast<size_t>(__builtin_amdgcn_readfirstlane(geo[kind * 4 + 1]));
-    const uint8_t* m = ps_matrix(p, ps_stage_layer(st, L), kind);
-    lw = rsrc(m + b0 * kBlockBytes, static_cast<uint32_t>(lcount) * kBlockBytes);
+    lnu = field(kind, 0);
+    const int u0 = field(kind, 1);
+    lG = field(kind, 2);
+    lnseg = field(kind, 3);
+    ltl = u0 / lnseg;
+    lseg = u0 - ltl * lnseg;
+    lk = 0;
+    const Geo gk = ps_geo(p, kind, wg, wave);
+    lw = rsrc(ps_matrix(p, ps_stage_layer(st, L), kind) + static_cast<size_t>(gk.t0) * lG * kBlockBytes,
+              static_cast<uint32_t>(gk.nt) * lG * kBlockBytes);
   };
   auto skip_empty_loads = [&]() {
-    while (lj >= lcount && lst < last) {
+    while (!lend && lk >= lnu) {
+      if (lst >= last) {  // the whole sequence is requested
+        lend = true;
+        lw = rsrc(nullptr, 0);
+        break;
+      }
       ++lst;
-      lj = 0;
-      if (gcount(lst) > 0) load_stage(lst);
-      else lcount = 0;
-    }
-    if (lj >= lcount) {  // the whole sequence is requested
-      lw = rsrc(nullptr, 0);
-      lj = 0;
+      if (units(lst) > 0) load_stage(lst);
     }
   };
-  if (gcount(0) > 0) load_stage(0);
+  // (the unit's offset goes into the per-lane offset, which the descriptor's
+  // range check covers)
+  auto load_unit = [&](u32x4& w0, u32x4& w1, u32x4& w2, u32x4& w3) {
+    const int o = (ltl * lG + lseg * kPsSeg) * kBlockBytes + lane * 16;
+    w0 = __builtin_amdgcn_raw_buffer_load_b128(lw, o, 0, kStreamOnce);
+    __builtin_amdgcn_sched_barrier(0);
+    w1 = __builtin_amdgcn_raw_buffer_load_b128(lw, o + kBlockBytes, 0, kStreamOnce);
+    __builtin_amdgcn_sched_barrier(0);
+    w2 = __builtin_amdgcn_raw_buffer_load_b128(lw, o + 2 * kBlockBytes, 0, kStreamOnce);
+    __builtin_amdgcn_sched_barrier(0);
+    w3 = __builtin_amdgcn_raw_buffer_load_b128(lw, o + 3 * kBlockBytes, 0, kStreamOnce);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!lend) {
+      ++lk;
+      if (++lseg == lnseg) {
+        lseg = 0;
+        ++ltl;
+      }
+    }
+    skip_empty_loads();
+  };
+  if (units(0) > 0) load_stage(0);
   skip_empty_loads();
 
-  // The ring. Loads are issued in the order their slots are consumed (the
-  // scheduling barriers keep the compiler from reordering them), so the wait
-  // before a slot is for its own load only.
+  // The ring, one unit (kPsSeg blocks) per step. Loads are issued in the
+  // order their slots are consumed (the scheduling barriers keep the compiler
+  // from reordering them), so the wait before a unit is for its own loads.
   u32x4 wv[kPsRing];
 #pragma unroll
-  for (int u = 0; u < kPsRing; ++u) {
-    wv[u] = __builtin_amdgcn_raw_buffer_load_b128(lw, lane * 16, lj * kBlockBytes, kStreamOnce);
-    __builtin_amdgcn_sched_barrier(0);
-    ++lj;
-    skip_empty_loads();
-  }
+  for (int k = 0; k < kPsRingUnits; ++k) load_unit(wv[4 * k], wv[4 * k + 1], wv[4 * k + 2], wv[4 * k + 3]);
 
-  // compute cursor: stage, blocks left, the (tile, group) of the next block,
-  // and the stage's group scales in LDS (staged by the control wave)
+  // Compute cursor: stage, units left, (tile, segment) of the next unit, the
+  // stage's group scales in LDS (staged by the control wave).
   bool done = false;
-  int cst = 0, cleft = 0, cG = 1, cnseg = 1, ctl = 0, cg = 0, cu = -1;
+  int cst = 0, cleft = 0, cG = 1, cnseg = 1, ctl = 0, cseg = 0;
   const uint8_t* csc = s.sca;
-  f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto flush = [&]() {
-    if (!done && cu >= 0 && (lane & 15) == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s.part[cu * 16 + 4 * kb + i] = acc[i];
-    }
-    acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    cu = -1;
-  };
   auto enter_stage = [&](int st) {
     const int kind = ps_stage_kind(st, L);
-    cleft = gcount(st);
-    const int b0 = __builtin_amdgcn_readfirstlane(geo[kind * 4 + 1]);
-    cG = __builtin_amdgcn_readfirstlane(geo[kind * 4 + 2]);
-    cnseg = __builtin_amdgcn_readfirstlane(geo[kind * 4 + 3]);
-    const Geo gk = ps_geo(p, kind, wg, wave);
-    const int wb0 = b0 - gk.t0 * cG;  // first block within the workgroup's tiles
-    ctl = wb0 / cG;
-    cg = wb0 - ctl * cG;
+    cleft = field(kind, 0);
+    const int u0 = field(kind, 1);
+    cG = field(kind, 2);
+    cnseg = field(kind, 3);
+    ctl = u0 / cnseg;
+    cseg = u0 - ctl * cnseg;
     csc = (kind == K_O || kind == K_D) ? s.scb : s.sca;
   };
   // the ends of the current stage and of every empty stage after it
   auto end_stages = [&]() {
-    flush();
     for (;;) {
       const int nb = ps_end_barriers(ps_stage_kind(cst, L));
       for (int b = 0; b < nb; ++b) ps_barrier();
@@ -402,38 +416,56 @@ __device__ __forceinline__ void ps_streaming(const PsParams& p, const PsLds& s, 
         return;
       }
       ++cst;
-      if (gcount(cst) > 0) break;
+      if (units(cst) > 0) break;
     }
     enter_stage(cst);
   };
+  // one unit: kPsSeg blocks of tile ctl, groups g0 .. g0 + kPsSeg - 1 (those
+  // past the tile's last group, if any, dropped); its partial sums into LDS
+  auto compute_unit = [&](const u32x4& w0, const u32x4& w1, const u32x4& w2, const u32x4& w3) {
+    const int g0 = cseg * kPsSeg;
+    const int len = min(kPsSeg, cG - g0);
+    const half_t* xg = s.xs + g0 * kGroup + kb * 32;
+    const uint8_t* sg = csc + (ctl * cG + g0) * 32 + kb * 8;
+    f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto blk = [&](const u32x4& w, int i) {
+      scale_acc(acc, ps_block(w, xg + i * kGroup, magic, nbias), *reinterpret_cast<const u32x2*>(sg + 32 * i));
+    };
+    if (len == kPsSeg) {
+      blk(w0, 0);
+      blk(w1, 1);
+      blk(w2, 2);
+      blk(w3, 3);
+    } else {  // a tile's short last segment (len >= 1)
+      blk(w0, 0);
+      if (len > 1) blk(w1, 1);
+      if (len > 2) blk(w2, 2);
+    }
+    if ((lane & 15) == 0) {
+      float* dst = s.part + (ctl * cnseg + cseg) * 16 + 4 * kb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = acc[i];
+    }
+  };
   ps_barrier();  // the first stage's input is staged
-  if (gcount(0) > 0) enter_stage(0);
+  if (units(0) > 0) enter_stage(0);
   else end_stages();
 
   for (int pass = 0; pass < passes; ++pass) {
 #pragma unroll
-    for (int u = 0; u < kPsRing; ++u) {
-      const int unit = ctl * cnseg + (cg >> 2);
-      if (unit != cu) {
-        flush();
-        cu = unit;
+    for (int k = 0; k < kPsRingUnits; ++k) {
+      if (!done) compute_unit(wv[4 * k], wv[4 * k + 1], wv[4 * k + 2], wv[4 * k + 3]);
+      load_unit(wv[4 * k], wv[4 * k + 1], wv[4 * k + 2], wv[4 * k + 3]);
+      if (!done) {
+        if (++cseg == cnseg) {
+          cseg = 0;
+          ++ctl;
+        }
+        if (--cleft == 0) end_stages();
       }
-      const int xo = cg * 128 + kb * 32;
-      const u32x2 sc = *reinterpret_cast<const u32x2*>(csc + (ctl * cG + cg) * 32 + kb * 8);
-      const f4 d = ps_block(wv[u], s.xs + xo, magic, nbias);
-      scale_acc(acc, d, sc);
-      wv[u] = __builtin_amdgcn_raw_buffer_load_b128(lw, lane * 16, lj * kBlockBytes, kStreamOnce);
-      __builtin_amdgcn_sched_barrier(0);
-      ++lj;
-      skip_empty_loads();
-      if (++cg == cG) {
-        cg = 0;
-        ++ctl;
-      }
-      if (--cleft == 0) end_stages();
     }
   }
-  if (!done) end_stages();  // (no block at all in any stage)
+  if (!done) end_stages();  // (no unit at all in any stage)
 }
 
 // ---------------------------------------------------------------- attention waves
@@ -872,6 +904,7 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
     if (l + 1 < L) ps_dma_scales(p, s.sca, K_QKV, l + 1);
     else ps_dma_scales(p, s.sca, K_LM, l);
     {
+      // a tile's 8 outputs: SwiGLU of its gate and up rows, pre-scaled
       const Geo gg = ps_geo(p, K_GU, wg, 0);
       for (int i = lane; i < gg.nt * 8; i += 64) {
         const int tl = i / 8, rr = i & 7;

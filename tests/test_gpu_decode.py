@@ -216,10 +216,10 @@ def test_split_attention_long_context(tiny):
 
 def test_split_attention_many_splits(tiny):
     """Batch 1 at a 2500-token context (157 pages): the persistent step splits
-    each KV head's pages four ways (40 pages per workgroup, 10 per attention
-    wave), and the last split to finish merges the four in LDS in two chunks
-    (three splits' partials fit its staging area at this shape). Logits and
-    tokens against the oracle."""
+    each KV head's pages 40 ways (4 pages per workgroup, one per attention
+    wave), and every workgroup merges two outputs over the 40 splits (the tiny
+    model's 512 outputs over 256 workgroups), ten per lane in three batches of
+    loads. Logits and tokens against the oracle."""
     om, dm = tiny
     prompt = synth.prompt_ids(2500, SHAPE.vocab, seed=61)
     say("tiny 2500-token context run")

@@ -12,8 +12,9 @@ over the full vocabulary at every generated step.
   chunked prefill (one chunk), then graph-replayed decode steps at contexts
   513-592 over the benchmark's 52-page table. With one kernel per stage,
   attention splits the pages over 13 workgroups per KV head (9-10 of them
-  live) and the combine kernel merges them; the persistent batch-1 step takes
-  one split of up to 48 pages per KV head.
+  live) and the combine kernel merges them; the persistent batch-1 step splits
+  each KV head's 33-38 live pages 9-10 ways (4 pages per workgroup, one per
+  attention wave) and every workgroup merges its share of the outputs.
 
 Every test runs in both step modes ("auto": batch 1 as the persistent
 whole-step kernel; "kernels": one kernel per stage).

@@ -183,8 +183,7 @@ struct PsParams {
   // workspace: hand-off flags, counters and buffers
   int* xflag;                       // [8][64] per-workgroup epochs, one row per XCD
   int* xcdflag;                     // [8][16] per-XCD epochs
-  int* cnt;                         // [16][16] split counters per KV head; row 14: per-XCD slot
-                                    // tickets; row 15: LM head
+  int* cnt;                         // [16][16] row 14: per-XCD slot tickets; row 15: LM head
   int* abort;
   uint16_t* hbuf;                   // [H] residual stream
   uint16_t* qbuf;                   // [nh * hd] q after RoPE

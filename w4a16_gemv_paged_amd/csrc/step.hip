@@ -474,12 +474,14 @@ struct AttPlan {
   int len, npages, per, S;  // context length, pages, pages per split, splits per KV head
 };
 
-// Splits of at most kPsSplitPages pages (a multiple of the attention waves),
-// as few as that allows: a split's pages are dealt to the workgroup's
-// attention waves in turn, and more than one split per KV head costs a merge
-// across workgroups. At most kPsMaxSplits splits per KV head and one
-// workgroup per split; a split then holds up to 64 pages per wave.
-constexpr int kPsSplitPages = 48;
+// Splits of kPsSplitPages pages (one per attention wave) while there are
+// workgroups for them: a split's pages are dealt to the workgroup's attention
+// waves in turn, and a wave's pages are a chain of load latencies (two pages
+// in flight), while more splits cost only the merge spread over all
+// workgroups (one hand-off and a few loads per lane). At most kPsMaxSplits
+// splits per KV head and one workgroup per split; longer contexts take more
+// pages per split, up to 64 per wave.
+constexpr int kPsSplitPages = 4;
 __device__ __forceinline__ AttPlan ps_att_plan(int len, int nkv) {
   AttPlan a;
   a.len = len;
@@ -812,7 +814,7 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
       };
       if (ap.S == 1) {
         store_ao();
-      } else {
+      } else {  // this split's (output, max, sum) of each head
         float* part = p.apart + static_cast<int64_t>(j * kPsMaxSplits + sp) * REP * R;
 #pragma unroll
         for (int h = 0; h < REP; ++h) {
@@ -820,62 +822,65 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
           for (int c = 0; c < NPH; ++c) st_f_sc1(part + h * R + lane + 64 * c, Oh[h][c]);
           if (lane < 2) st_f_sc1(part + h * R + D + lane, lane == 0 ? Mh[h] : Lh[h]);
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        int old = 0;
-        if (lane == 0) old = __hip_atomic_fetch_add(p.cnt + j * 16, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        old = __builtin_amdgcn_readfirstlane(old);
-        if (old == ap.S - 1) {
-          // The last split of this KV head to finish merges them all. The
-          // splits' rows are brought into LDS (the staging area xs, gs, unused
-          // until the O stage's input is staged) as many at a time as fit and
-          // merged there; every chunk after the first rescales the running
-          // result.
-          if (lane == 0) st_sc1(p.cnt + j * 16, 0);
-          const float* pb = p.apart + static_cast<int64_t>(j * kPsMaxSplits) * REP * R;
-          float* buf = reinterpret_cast<float*>(s.xs);
-          const int cap = max(1, ((p.kmax + p.H) * 2) / (REP * R * 4));
+      }
+    }
+    if (ap.S > 1) {
+      // Every split is in memory: each workgroup merges its share of the
+      // outputs (m per workgroup) over the S splits. Lane i + m g (i < m
+      // outputs, g < 4 groups) takes splits g, g + 4, ... of output i, four at
+      // a time (their loads issued together); the four groups are then merged
+      // in group order.
+      ps_sync(p, ++epoch, x, li);
+      constexpr int R = D + 4;
+      const int nout = p.nh * D;
+      const int m = (nout + kPsWG - 1) / kPsWG;  // outputs per workgroup (4 m <= 64: nh * D <= 4096)
+      const int i = lane % m, g = lane / m;
+      const int o = wg * m + i;
+      float M = -INFINITY, Ls = 0.0f, O = 0.0f;
+      if (g < 4 && o < nout) {
+        const int head = o / D, d = o % D, j = head / REP, h = head % REP;
+        const float* pb = p.apart + static_cast<int64_t>(j * kPsMaxSplits) * REP * R + h * R;
+        for (int q0 = g; q0 < ap.S; q0 += 16) {
+          float mq[4], lq[4], oq[4];
 #pragma unroll
-          for (int h = 0; h < REP; ++h) {
-            Mh[h] = -INFINITY;
-            Lh[h] = 0.0f;
-#pragma unroll
-            for (int c = 0; c < NPH; ++c) Oh[h][c] = 0.0f;
-          }
-          for (int q0 = 0; q0 < ap.S; q0 += cap) {
-            const int nq = min(cap, ap.S - q0);
-            const int n16 = nq * REP * R / 4;  // 16-byte items
-            for (int c = 0; c * 64 < n16; ++c) {
-              const int item = c * 64 + lane;
-              if (item < n16) __builtin_amdgcn_global_load_lds(pb + q0 * REP * R + item * 4, buf + c * 256, 16, 0, kSc1);
+          for (int u = 0; u < 4; ++u) {
+            const int q = q0 + 4 * u;
+            mq[u] = -INFINITY;
+            lq[u] = oq[u] = 0.0f;
+            if (q < ap.S) {
+              const float* r = pb + static_cast<int64_t>(q) * REP * R;
+              mq[u] = ld_f_sc1(r + D);
+              lq[u] = ld_f_sc1(r + D + 1);
+              oq[u] = ld_f_sc1(r + d);
             }
-            __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll
-            for (int h = 0; h < REP; ++h) {
-              float M = Mh[h];
-              for (int q = 0; q < nq; ++q) M = fmaxf(M, buf[(q * REP + h) * R + D]);
-              const float sc = Mh[h] == -INFINITY ? 0.0f : exp2f(Mh[h] - M);
-              float Ls = Lh[h] * sc;
-              float O[NPH];
-#pragma unroll
-              for (int c = 0; c < NPH; ++c) O[c] = Oh[h][c] * sc;
-              for (int q = 0; q < nq; ++q) {
-                const float* r = buf + (q * REP + h) * R;
-                const float mq = r[D];
-                const float f = mq == -INFINITY ? 0.0f : exp2f(mq - M);
-                Ls = fmaf(f, r[D + 1], Ls);
-#pragma unroll
-                for (int c = 0; c < NPH; ++c) O[c] = fmaf(f, r[lane + 64 * c], O[c]);
-              }
-              Mh[h] = M;
-              Lh[h] = Ls;
-#pragma unroll
-              for (int c = 0; c < NPH; ++c) Oh[h][c] = O[c];
-            }
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the chunk is read before the next one lands
           }
-          store_ao();
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (mq[u] != -INFINITY) {
+              const float Mn = fmaxf(M, mq[u]);
+              const float a = M == -INFINITY ? 0.0f : exp2f(M - Mn), b = exp2f(mq[u] - Mn);
+              Ls = Ls * a + lq[u] * b;
+              O = O * a + oq[u] * b;
+              M = Mn;
+            }
+          }
         }
       }
+      // the four groups of output i, in group order (lanes i, i + m, ...)
+      float Mt = __shfl(M, i), Lt = __shfl(Ls, i), Ot = __shfl(O, i);
+#pragma unroll
+      for (int gg = 1; gg < 4; ++gg) {
+        const float mg = __shfl(M, i + gg * m), lg = __shfl(Ls, i + gg * m), og = __shfl(O, i + gg * m);
+        if (mg != -INFINITY) {
+          const float Mn = fmaxf(Mt, mg);
+          const float a = Mt == -INFINITY ? 0.0f : exp2f(Mt - Mn), b = exp2f(mg - Mn);
+          Lt = Lt * a + lg * b;
+          Ot = Ot * a + og * b;
+          Mt = Mn;
+        }
+      }
+      if (g == 0 && o < nout)
+        st_h_sc1(hm(p.ao) + o, ps_prescale(static_cast<half_t>(Lt > 0.0f ? Ot / Lt : 0.0f), o % D));
     }
     ps_sync(p, ++epoch, x, li);
     ps_dma(s.xs, hc(p.ao), p.nh * D, true);

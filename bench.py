@@ -6,18 +6,23 @@ random-init (synthetic) weights and prompts.
 Headline (the printed JSON line): batch-1 greedy decode, 512-token random
 prompt fed through the chunked prefill (timed: the time to first token), then
 the step replayed as one HIP graph per token; ``value`` = tokens/s over exactly
---steps timed replays (after --warmup).
-The same line also carries the batch-8 decode (ragged contexts uniform in
-[128, 16384], 128 steps), the W4A16 GEMV sweep at the 7B projection shapes
-(GB/s and fraction of the 8 TB/s HBM peak; beside each, the INT8-activation
-variant with its quantisation fused into the GEMV and as a separate kernel),
-the roofline of the dominant
-kernel (the gate/up GEMV + SwiGLU) and the CPU oracle timed on a bounded
-sample.
+--steps timed replays (after --warmup). At batch 1 the step is the persistent
+whole-step kernel; the same tokens are then timed with one kernel per stage.
+The same line also carries batch 1 at contexts 4097 and 32767 in both step
+modes, the batch-8 decode (ragged contexts uniform in [128, 16384], 128 steps),
+the attention sweep (the attention and combine kernels at batch 1 over 511,
+4097 and 32767 tokens and at batch 8 over ragged lengths in [1, 32767]), the
+W4A16 GEMV sweep at the 7B projection shapes (GB/s and fraction of the 8 TB/s
+HBM peak; beside each, the INT8-activation variant with its quantisation fused
+into the GEMV and as a separate kernel), the roofline of the dominant kernel
+(the gate/up GEMV + SwiGLU) and the CPU oracle timed on bounded samples.
 
 Modes (for profiling runs): --mode roofline launches only the gate/up GEMV of
 28 distinct weight copies; --mode copy runs a 1 GiB device copy (the
-calibration for the FETCH_SIZE / WRITE_SIZE counters).
+calibration for the FETCH_SIZE / WRITE_SIZE counters); --mode stepkern runs a
+few batch-1 steps at context 520 with one kernel per stage and as the
+persistent kernel, then the attention kernels at 4097 and 32767 tokens (for
+per-kernel counters).
 """
 from __future__ import annotations
 
@@ -217,6 +222,175 @@ def gemv_sweep(stream):
     return out, agg
 
 
+def attn_bytes(shape, lens) -> int:
+    """Algorithmic bytes of one layer's decode attention: the K and V rows of
+    every cached token (fp16), q in and the output out (fp16)."""
+    kv = 2 * shape.n_kv_heads * shape.head_dim * 2 * int(sum(int(x) for x in lens))
+    return kv + 2 * 2 * len(lens) * shape.n_heads * shape.head_dim
+
+
+def attention_sweep(dm, shape, stream, reps: int = 4):
+    """The decode attention and combine kernels of one layer (nq_attn_decode),
+    timed back to back over the 28 layers of a random-filled pool (every call a
+    different layer's pages, as in the step): batch 1 at 511, 4097 and 32767
+    cached tokens, and batch 8 over lengths uniform in [1, 32767] (seed 6)."""
+    import numpy as np
+    import torch
+    import synth
+    import w4a16_gemv_paged_amd as nq
+    from w4a16_gemv_paged_amd.engine import KVCache
+    cases = [("B1_511", [511]), ("B1_4097", [4097]), ("B1_32767", [32767]),
+             ("B8_ragged_1_32767_seed6", synth.ragged_lengths(8, 1, 32767, seed=6).tolist())]
+    sid = stream.cuda_stream
+    out = []
+    for name, lens in cases:
+        B = len(lens)
+        max_pages = max((int(x) + 15) // 16 for x in lens)
+        pt, total = synth.decode_page_tables(B, max_pages, seed=3)
+        kv = KVCache(dm, total, poison=False)
+        synth.fill_device_normal(kv.pool.view(torch.float16), seed=7)
+        q = torch.randn(B, shape.n_heads, shape.head_dim, dtype=torch.float16, device="cuda")
+        o = torch.empty_like(q)
+        ptd = torch.from_numpy(pt).cuda()
+        ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        wsb = nq.nq_attn_workspace_bytes(dm.cfg, B, max_pages)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        fn = lambda j: nq.nq_attn_decode(kv.handle, j % shape.layers, B, q, ptd, max_pages, ld, o, ws, wsb, err,
+                                         stream=stream)
+        for j in range(shape.layers):
+            fn(j)
+        mean_s, b2b_s = time_launches(fn, shape.layers, stream, reps=reps)
+        nq.nq_check_device_error(err)
+        nb = attn_bytes(shape, lens)
+        out.append({"case": name, "batch": B, "lens": [int(x) for x in lens], "max_pages": max_pages,
+                    "bytes": nb, "us": round(b2b_s * 1e6, 2), "GBs": round(nb / b2b_s / 1e9, 1),
+                    "frac": round(nb / b2b_s / PEAK_HBM, 4), "event_pair_us": round(mean_s * 1e6, 2)})
+        log(f"attention {name}: {b2b_s * 1e6:.2f} us, {nb / b2b_s / 1e9:.0f} GB/s")
+        kv.close()
+        del kv, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def context_sweep(dm, shape, stream, contexts=(4097, 32700), steps: int = 32):
+    """Batch-1 decode at long contexts over a random-filled pool (timing only:
+    the tokens are not a real continuation), in both step modes: ms per token
+    over ``steps`` graph replays."""
+    import torch
+    import synth
+    from w4a16_gemv_paged_amd.engine import KVCache, Stepper
+    out = []
+    for ctx in contexts:
+        max_pages = (ctx + steps + 8 + 15) // 16
+        pt, total = synth.decode_page_tables(1, max_pages, seed=3)
+        kv = KVCache(dm, total, poison=False)
+        synth.fill_device_normal(kv.pool.view(torch.float16), seed=7)
+        row = {"context": ctx}
+        for mode in ("auto", "kernels"):
+            dm.set_step_mode(mode)
+            st = Stepper(dm, kv, pt)
+            with torch.cuda.stream(stream):
+                st.set_pos([ctx])
+                st.set_tokens([17])
+                n = st.capture(stream)
+                for _ in range(4):
+                    st.replay(stream)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(steps):
+                    st.replay(stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                st.check(stream)
+            row[mode] = {"ms_per_token": round(e0.elapsed_time(e1) / steps, 4), "kernels_per_step": n}
+            st.close()
+            del st
+        dm.set_step_mode("auto")
+        log(f"B=1 at context {ctx}: persistent {row['auto']['ms_per_token']} ms, "
+            f"kernels {row['kernels']['ms_per_token']} ms")
+        out.append(row)
+        kv.close()
+        del kv
+        torch.cuda.empty_cache()
+    return out
+
+
+def host_info() -> dict:
+    """BLAS the oracle's NumPy links, host RAM and this process's peak resident set."""
+    import resource
+    import numpy as np
+    info = {"blas": None, "ram_total_gb": None,
+            "peak_rss_gb": round(resource.getrusage(resource.RUSAGE_SELF).ru_maxrss / 2**20, 2)}
+    try:
+        cfg = np.show_config(mode="dicts")
+        blas = cfg.get("Build Dependencies", {}).get("blas", {})
+        info["blas"] = f"{blas.get('name')} {blas.get('version')}"
+    except Exception:
+        pass
+    try:
+        import psutil
+        info["ram_total_gb"] = round(psutil.virtual_memory().total / 2**30, 1)
+    except Exception:
+        pass
+    return info
+
+
+def cpu_rows(shape, budget_s: float = 4.0) -> dict:
+    """The oracle's building blocks timed on the host cores (median of up to 5
+    runs within ``budget_s`` each): the W4A16 GEMV (dequantise + float64
+    product) at the four projection shapes for B = 1 and 4, the decode
+    attention of one layer at 511, 4097 and 32767 cached tokens, and one
+    decode step of the tiny config (all layers and the LM head)."""
+    import numpy as np
+    import synth
+    import oracle
+    from oracle.model import OracleModel, ContiguousKV, decode_step
+
+    def med(fn):
+        ts = []
+        t_end = time.perf_counter() + budget_s
+        while len(ts) < 5 and (len(ts) < 1 or time.perf_counter() < t_end):
+            t = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t)
+        return sorted(ts)[len(ts) // 2], len(ts)
+
+    rows = {"gemv": [], "attention": [], "tiny": None}
+    for (k, n) in GEMV_ROTATION:
+        q, s16 = oracle.quantize_w4(synth.gemv_weight(k, n, seed=0))
+        for b in (1, 4):
+            x = synth.activations(b, k, seed=1)
+            t, m = med(lambda: oracle.gemv_w4a16(q, s16, x))
+            rows["gemv"].append({"K": k, "N": n, "B": b, "s": round(t, 4), "runs": m})
+        del q, s16
+    d, nh, nkv = shape.head_dim, shape.n_heads, shape.n_kv_heads
+    rng = np.random.default_rng(5)
+    for L in (511, 4097, 32767):
+        qv = rng.standard_normal((nh, d)).astype(np.float16)
+        kk = rng.standard_normal((L, nkv, d)).astype(np.float16)
+        vv = rng.standard_normal((L, nkv, d)).astype(np.float16)
+        t, m = med(lambda: oracle.attend(qv, kk, vv))
+        rows["attention"].append({"len": L, "s": round(t, 4), "runs": m})
+    tiny = synth.TINY
+    layers = [synth.layer_params(tiny, i, seed=0) for i in range(tiny.layers)]
+    om = OracleModel.build(tiny, layers, synth.head_params(tiny, seed=0))
+    cache = ContiguousKV(tiny.layers, tiny.n_kv_heads, tiny.head_dim)
+    pos = [0]
+
+    def tiny_step():
+        decode_step(om, [cache], [17], [pos[0]])
+        pos[0] += 1
+
+    t, m = med(tiny_step)
+    rows["tiny"] = {"config": tiny.name, "s_per_token": round(t, 4), "runs": m,
+                    "context": "0..%d (a fresh contiguous cache)" % (m - 1)}
+    rows["cores"] = len(os.sched_getaffinity(0))
+    rows.update(host_info())
+    return rows
+
+
 def cpu_baseline(shape, head, sample_layers: int = 1, head_frac: int = 8, budget_s: float = 10.0, ctx: int = 512):
     """The oracle's decode step timed on the host cores on a bounded sample:
     ``sample_layers`` of the layers and 1/``head_frac`` of the LM-head rows, at
@@ -280,7 +454,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=248)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--mode", choices=["full", "roofline", "copy"], default="full")
+    ap.add_argument("--mode", choices=["full", "roofline", "copy", "stepkern"], default="full")
     ap.add_argument("--skip-b8", action="store_true")
     ap.add_argument("--skip-sweep", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
@@ -323,6 +497,29 @@ def main() -> int:
         with torch.cuda.stream(stream):
             r = gate_up_roofline(layers, shape.hidden, shape.intermediate, stream, reps=4)
         print(json.dumps({"mode": "roofline", "roofline": r}), flush=True)
+        return 0
+
+    if args.mode == "stepkern":
+        head = synth.head_params(shape, seed=0)
+        dm = DeviceModel(shape, lambda l: synth.layer_params(shape, l, seed=0), head, max_batch=8, max_pos=32768)
+        pt, total = synth.decode_page_tables(1, 40, seed=3)
+        kv = KVCache(dm, total, poison=False)
+        synth.fill_device_normal(kv.pool.view(torch.float16), seed=7)
+        for mode in ("kernels", "auto"):
+            dm.set_step_mode(mode)
+            st = Stepper(dm, kv, pt)
+            st.set_pos([520])
+            st.set_tokens([17])
+            with torch.cuda.stream(stream):
+                for _ in range(4):
+                    st.step(stream)
+                torch.cuda.synchronize()
+                st.check(stream)
+            st.close()
+        kv.close()
+        with torch.cuda.stream(stream):
+            att = attention_sweep(dm, shape, stream, reps=1)
+        print(json.dumps({"mode": "stepkern", "steps_per_mode": 4, "context": 520, "attention": att}), flush=True)
         return 0
 
     # ------------------------------------------------------------------ model
@@ -393,12 +590,50 @@ def main() -> int:
     st.close()
     kv1.close()
     del st, kv1
+    # the same prompt, page table and timed contexts with one kernel per stage
+    dm.set_step_mode("kernels")
+    kv1 = KVCache(dm, total, poison=False)
+    st = Stepper(dm, kv1, pt, hist_len=need + 1)
+    with torch.cuda.stream(stream):
+        pf = Prefill(dm, kv1, P)
+        pf.run(prompt, st.page_table[0], 0, next_token=st.tokens[0:1], pos_out=st.pos[0:1], stream=stream)
+        pf.check(stream)
+        del pf
+        n_kernels_k = st.capture(stream)
+        for _ in range(W):
+            st.replay(stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            st.replay(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_b1_k = e0.elapsed_time(e1) / K
+        st.check(stream)
+    gen_k = st.hist.cpu().numpy()[0][P + 1:P + 1 + W + K]
+    dm.set_step_mode("auto")
+    b1_kernels = {"ms_per_token": round(ms_b1_k, 4), "tok_s": round(1e3 / ms_b1_k, 1), "kernels_per_step": n_kernels_k,
+                  "context_during_timing": [ctx0, ctx0 + K],
+                  "tokens_equal_to_persistent": int(np.sum(gen_k == gen)), "tokens_compared": int(len(gen))}
+    log(f"B=1 with one kernel per stage ({n_kernels_k} kernels): {ms_b1_k:.3f} ms/token; "
+        f"{b1_kernels['tokens_equal_to_persistent']}/{len(gen)} tokens as the persistent step's")
+    st.close()
+    kv1.close()
+    del st, kv1
 
     # ------------------------------------------------------------------ roofline of the dominant kernel
     with torch.cuda.stream(stream):
         roof = gate_up_roofline([(L["gate_up"], L["g2"]) for L in dm.layers], shape.hidden, shape.intermediate,
                                 stream, reps=10)
     log(f"gate/up GEMV: {roof['back_to_back_us']} us/launch, {roof['achieved']} GB/s ({roof['frac'] * 100:.1f}%)")
+
+    # ------------------------------------------------------------------ long contexts, attention
+    ctx_sweep = att_sweep = None
+    if not args.skip_sweep:
+        ctx_sweep = context_sweep(dm, shape, stream)
+        with torch.cuda.stream(stream):
+            att_sweep = attention_sweep(dm, shape, stream)
 
     # ------------------------------------------------------------------ B = 8
     b8 = None
@@ -451,6 +686,9 @@ def main() -> int:
         log("timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(shape, head)
         log(f"oracle: {cpu['s_per_token']} s/token on {cpu['cores']} cores")
+        cpu["rows"] = cpu_rows(shape)
+        log(f"oracle rows: {len(cpu['rows']['gemv'])} GEMV, {len(cpu['rows']['attention'])} attention, tiny "
+            f"{cpu['rows']['tiny']['s_per_token']} s/token; BLAS {cpu['rows']['blas']}")
 
     wb = step_weight_bytes(shape)
     res = {
@@ -462,9 +700,14 @@ def main() -> int:
                    "context_during_timing": [ctx0, ctx0 + K], "weights": "int4 symmetric g128, fp16 scales",
                    "activations": "fp16, fp32 accumulation", "kernels_per_step": n_kernels},
         "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "traffic_source": ("profiles/gemv_gate_up_swiglu_7b_b1_pmc.md: rocprofv3 FETCH_SIZE / WRITE_SIZE runs on "
+                           "the same GEMV source hash (not measured in this run; null when the hash differs)"),
         "cpu_baseline": cpu,
         "ms_per_token_b1_events": round(ms_b1_events, 4),
         "ms_per_token_b1_eager": round(ms_eager, 4),
+        "b1_kernel_per_stage": b1_kernels,
+        "b1_context_sweep": ctx_sweep,
+        "attention_sweep": att_sweep,
         "step_weight_bytes": wb,
         "step_roofline_ms": round(wb / PEAK_HBM * 1e3, 4),
         "step_roofline_frac": round(wb / PEAK_HBM * 1e3 / ms_b1, 4),

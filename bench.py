@@ -22,7 +22,8 @@ Modes (for profiling runs): --mode roofline launches only the gate/up GEMV of
 calibration for the FETCH_SIZE / WRITE_SIZE counters); --mode stepkern runs a
 few batch-1 steps at context 520 with one kernel per stage and as the
 persistent kernel, then the attention kernels at 4097 and 32767 tokens (for
-per-kernel counters).
+per-kernel counters); --mode stagetrace runs the batch-1 configuration's
+persistent step with its stage stamps on and prints the per-stage timeline.
 """
 from __future__ import annotations
 
@@ -317,6 +318,70 @@ def context_sweep(dm, shape, stream, contexts=(4097, 32700), steps: int = 32):
     return out
 
 
+STAGE_EVENTS = ["QKV partials in", "QKV hand-off: arrive", "QKV hand-off: all arrived", "attention partials in",
+                "attention hand-off: arrive", "attention hand-off: all arrived", "O partials in", "O hand-off: arrive",
+                "O hand-off: all arrived", "gate/up partials in", "gate/up hand-off: arrive",
+                "gate/up hand-off: all arrived", "down partials in", "down hand-off: arrive", "down hand-off: all arrived",
+                "next stage's input staged"]
+
+
+def stage_trace(shape, stream, steps: int = 16):
+    """The batch-1 configuration (512-token prompt through the prefill, 52-page
+    table) stepped with the persistent kernel's stage stamps on: per event, the
+    time since the layer's start (the previous layer's last event), median
+    over steps and layers 1..L-2 of the median and of the maximum over the 256
+    workgroups; the layer, LM head and whole-step durations."""
+    import numpy as np
+    import torch
+    import synth
+    from w4a16_gemv_paged_amd.engine import DeviceModel, KVCache, Stepper, Prefill
+    head = synth.head_params(shape, seed=0)
+    dm = DeviceModel(shape, lambda l: synth.layer_params(shape, l, seed=0), head, max_batch=8, max_pos=32768)
+    P, L = 512, shape.layers
+    pt, total = synth.decode_page_tables(1, 52, seed=3)
+    kv = KVCache(dm, total, poison=False)
+    st = Stepper(dm, kv, pt, hist_len=P + steps + 16)
+    buf = torch.full((256 * (L + 1) * 16,), -1, dtype=torch.int64, device="cuda")
+    samples = []
+    with torch.cuda.stream(stream):
+        pf = Prefill(dm, kv, P)
+        pf.run(synth.prompt_ids(P, shape.vocab, seed=2), st.page_table[0], 0, next_token=st.tokens[0:1],
+               pos_out=st.pos[0:1], stream=stream)
+        pf.check(stream)
+        dm.set_step_trace(buf)
+        st.capture(stream)
+        for i in range(steps + 4):
+            st.replay(stream)
+            torch.cuda.synchronize()
+            if i >= 4:
+                samples.append(buf.cpu().numpy().reshape(256, L + 1, 16).copy())
+        st.check(stream)
+        dm.set_step_trace(None)
+    st.close()
+    kv.close()
+    dm.close()
+    ev_med = [[] for _ in range(16)]
+    ev_max = [[] for _ in range(16)]
+    layer_us, lm_us, step_us = [], [], []
+    for t in samples:
+        t = t.astype(np.float64) / 100.0                      # 100 MHz counter -> us
+        for l in range(1, L - 1):
+            start = t[:, l - 1, 15]
+            for e in range(16):
+                d = t[:, l, e] - start
+                ev_med[e].append(float(np.median(d)))
+                ev_max[e].append(float(np.max(d)))
+            layer_us.append(float(np.median(t[:, l, 15] - t[:, l - 1, 15])))
+        lm_us.append(float(np.median(t[:, L, 2] - t[:, L - 1, 15])))
+        step_us.append(float(np.max(t[:, L, 2]) - np.min(t[:, L, 0])))
+    med = lambda v: round(float(np.median(v)), 2)
+    return {"mode": "stagetrace", "steps": len(samples), "context": [P + 4, P + 4 + len(samples)],
+            "events": [{"event": STAGE_EVENTS[e], "us_since_layer_start_median_wg": med(ev_med[e]),
+                        "us_since_layer_start_slowest_wg": med(ev_max[e])} for e in range(16)],
+            "layer_us": med(layer_us), "lm_head_and_greedy_us": med(lm_us), "step_us": med(step_us),
+            "first_layer_start_us": med([float(np.median(t[:, 0, 0] - t[:, L, 0])) / 100.0 for t in samples])}
+
+
 def host_info() -> dict:
     """BLAS the oracle's NumPy links, host RAM and this process's peak resident set."""
     import resource
@@ -454,7 +519,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=248)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--mode", choices=["full", "roofline", "copy", "stepkern"], default="full")
+    ap.add_argument("--mode", choices=["full", "roofline", "copy", "stepkern", "stagetrace"], default="full")
     ap.add_argument("--skip-b8", action="store_true")
     ap.add_argument("--skip-sweep", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
@@ -497,6 +562,10 @@ def main() -> int:
         with torch.cuda.stream(stream):
             r = gate_up_roofline(layers, shape.hidden, shape.intermediate, stream, reps=4)
         print(json.dumps({"mode": "roofline", "roofline": r}), flush=True)
+        return 0
+
+    if args.mode == "stagetrace":
+        print(json.dumps(stage_trace(shape, stream)), flush=True)
         return 0
 
     if args.mode == "stepkern":

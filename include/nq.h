@@ -513,6 +513,24 @@ nq_status nq_model_set_step_mode(nq_model* m, int32_t mode);
  * for the persistent kernel), or -1 for invalid arguments. Host only. */
 int32_t nq_step_kernels(const nq_model* m, int32_t batch, int32_t max_pages);
 
+/*
+ * Measurement hook of the persistent step: when device_buf is set, every
+ * persistent step enqueued (or captured) afterwards writes, per workgroup w of
+ * 256 and row r of layers + 1, 16 uint64 stamps of the GPU's constant 100 MHz
+ * realtime counter at buf[(w * (layers + 1) + r) * 16 + e]. Row l < layers,
+ * events 0-15: the QKV partials are in, before and after the QKV hand-off, the
+ * attention partials are in, before and after the attention hand-off, the O
+ * partials are in, before and after the O hand-off, the gate/up partials, before
+ * and after its hand-off, the down partials, before and after its hand-off, the
+ * next stage's input staged. Row layers, events 0-2: the workgroup's start, the
+ * LM head's partials are in, its last work done. Other entries are not
+ * written. bytes must be at least 256 * (layers + 1) * 16 * 8, device_buf 8-byte
+ * aligned device memory the caller owns; NULL turns the stamps off (the
+ * default). Steps of one kernel per stage write nothing. The stamps change
+ * no result.
+ */
+nq_status nq_model_set_step_trace(nq_model* m, uint64_t* device_buf, int64_t bytes);
+
 /* ---------------------------------------------------------- chunked prefill */
 
 /*

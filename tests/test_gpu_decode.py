@@ -252,6 +252,33 @@ def test_split_attention_batch8(tiny):
     np.testing.assert_array_equal(g["logits"].view(np.uint32), gpu["logits"].view(np.uint32))
 
 
+def test_stage_trace_changes_nothing(tiny):
+    """The persistent step's stage stamps (nq_model_set_step_trace) leave every
+    logit bitwise unchanged; after the run the buffer holds the last step's
+    stamps, in order within each workgroup (kernel start, 16 events per layer,
+    LM head partials, end). With one kernel per stage nothing is written."""
+    om, dm = tiny
+    prompt = synth.prompt_ids(20, SHAPE.vocab, seed=12)
+    say("trace off / on runs")
+    a = _run(dm, [prompt], 6, layers=False)
+    L = SHAPE.layers
+    buf = torch.full((256 * (L + 1) * 16,), -1, dtype=torch.int64, device="cuda")
+    dm.set_step_trace(buf)
+    try:
+        b = _run(dm, [prompt], 6, layers=False)
+    finally:
+        dm.set_step_trace(None)
+    np.testing.assert_array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32))
+    t = buf.cpu().numpy().reshape(256, L + 1, 16)
+    if dm.mode == "auto":
+        seq = np.concatenate([t[:, L, :1], t[:, :L, :].reshape(256, -1), t[:, L, 1:3]], axis=1)
+        assert np.all(seq > 0)
+        assert np.all(np.diff(seq, axis=1) >= 0)
+        assert np.all(t[:, L, 3:] == -1)
+    else:
+        assert np.all(t == -1)
+
+
 def test_model_from_container_decodes_identically(tiny, tmp_path):
     """The same weights through the packed-weight container (written once,
     memory-mapped and uploaded without repacking) decode bit for bit alike."""

@@ -253,6 +253,32 @@ def test_model_state_errors_without_gpu():
         nq.nq_model_destroy(m)
 
 
+def test_step_mode_and_trace_arguments_without_gpu():
+    """nq_model_set_step_mode takes the two modes only; nq_model_set_step_trace
+    takes NULL (off) or a buffer of at least 256 * (layers + 1) * 16 uint64,
+    8-byte aligned. The buffer is only recorded here, never touched."""
+    import synth
+    cfg = nq.NQConfig.from_shape(synth.TINY, 1, 64)
+    m = nq.nq_model_create(cfg)
+    try:
+        for mode in (nq.NQ_STEP_AUTO, nq.NQ_STEP_KERNELS):
+            nq.nq_model_set_step_mode(m, mode)
+        with pytest.raises(nq.NQError) as e:
+            nq.nq_model_set_step_mode(m, 7)
+        assert e.value.status == 1
+        need = 256 * (synth.TINY.layers + 1) * 16 * 8
+        fake = 1 << 20
+        nq.nq_model_set_step_trace(m, fake, need)
+        nq.nq_model_set_step_trace(m, None, 0)
+        for buf, nbytes in ((fake, need - 8), (fake + 4, need)):
+            with pytest.raises(nq.NQError) as e:
+                nq.nq_model_set_step_trace(m, buf, nbytes)
+            assert e.value.status == 1
+        assert nq.lib().nq_model_set_step_trace(None, None, 0) == 1
+    finally:
+        nq.nq_model_destroy(m)
+
+
 def test_static_attention_refuses_beyond_its_scratch_without_gpu():
     """nq_attn_decode_static checks the split partials against its fixed
     library scratch (NQ_ATTN_SCRATCH_BYTES) before it looks up or touches any

@@ -23,7 +23,7 @@ __all__ = [
     "nq_unpack_weights", "nq_unpack_weights_dev", "nq_gemv_w4a16", "nq_config_check",
     "nq_kv_pool_bytes", "nq_kv_alloc", "nq_kv_append", "nq_kv_free", "nq_attn_workspace_bytes",
     "nq_attn_decode", "nq_attn_decode_static", "NQ_ATTN_SCRATCH_BYTES", "nq_model_create",
-    "nq_model_set_step_mode", "nq_step_kernels", "NQ_STEP_AUTO", "NQ_STEP_KERNELS", "nq_model_bind_layer", "nq_model_bind_head",
+    "nq_model_set_step_mode", "nq_step_kernels", "nq_model_set_step_trace", "NQ_STEP_AUTO", "NQ_STEP_KERNELS", "nq_model_bind_layer", "nq_model_bind_head",
     "nq_rope_table_bytes", "nq_rope_table_fill", "nq_model_bind_rope", "nq_workspace_bytes",
     "nq_model_bind_workspace", "nq_model_destroy", "nq_decode_step", "nq_graph_capture",
     "nq_graph_launch", "nq_graph_kernel_count", "nq_graph_destroy", "nq_check_device_error",
@@ -127,6 +127,7 @@ _SIGS = {
     "nq_model_destroy": (None, [_P]),
     "nq_model_set_step_mode": (_I, [_P, _I]),
     "nq_step_kernels": (_I, [_P, _I, _I]),
+    "nq_model_set_step_trace": (_I, [_P, _P, ctypes.c_int64]),
     "nq_decode_step": (_I, [_P, _P, ctypes.POINTER(NQStepIO), _P]),
     "nq_graph_capture": (_I, [_P, _P, ctypes.POINTER(NQStepIO), _P, ctypes.POINTER(_P)]),
     "nq_graph_launch": (_I, [_P, _P]),
@@ -325,6 +326,10 @@ def nq_attn_prefill(kv, layer, n_q, start_pos, q, page_table, max_pages, out, er
 # ------------------------------------------------------------------ model, step, graph
 
 NQ_STEP_AUTO, NQ_STEP_KERNELS = 0, 1
+
+
+def nq_model_set_step_trace(model, buf, nbytes: int) -> None:
+    _check(lib().nq_model_set_step_trace(model, _ptr(buf), nbytes), "nq_model_set_step_trace")
 
 
 def nq_model_set_step_mode(model, mode: int) -> None:

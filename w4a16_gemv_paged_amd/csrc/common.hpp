@@ -193,6 +193,7 @@ struct PsParams {
   float* lmval;                     // [kPsWG] greedy partials
   int32_t* lmidx;
   int max_polls;                    // bound of every wait
+  unsigned long long* stage_trace;  // optional [kPsWG][L + 1][16] realtime stamps (see nq_model_set_step_trace)
 };
 size_t ps_lds_bytes(const PsParams& p);
 bool ps_supported(int head_dim, int n_heads, int n_kv);

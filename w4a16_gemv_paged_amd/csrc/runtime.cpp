@@ -24,6 +24,7 @@ struct nq_model {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   int32_t step_mode = NQ_STEP_AUTO;
+  uint64_t* step_trace = nullptr;   // stage stamps of the persistent step (measurement), or null
 };
 
 struct nq_kv {
@@ -216,6 +217,7 @@ int enqueue_step_persistent(nq_model* m, nq_kv* kv, const nq_step_io* io, hipStr
   p.qbuf = static_cast<uint16_t*>(w.ps_q);
   p.ao = static_cast<uint16_t*>(w.ps_ao);
   p.act = static_cast<uint16_t*>(w.ps_act);
+  p.stage_trace = reinterpret_cast<unsigned long long*>(m->step_trace);
   p.apart = w.apart;
   p.lmval = w.lmval;
   p.lmidx = w.lmidx;
@@ -871,6 +873,20 @@ nq_status nq_model_bind_workspace(nq_model* m, void* ws, size_t bytes) {
   if (!aligned16(ws)) return fail(NQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   m->ws = ws;
   m->ws_bytes = bytes;
+  return NQ_OK;
+}
+
+nq_status nq_model_set_step_trace(nq_model* m, uint64_t* device_buf, int64_t bytes) {
+  if (!m) return fail(NQ_ERR_INVALID_ARG, "null model");
+  if (!device_buf) {
+    m->step_trace = nullptr;
+    return NQ_OK;
+  }
+  const int64_t need = static_cast<int64_t>(kPsWG) * (m->cfg.layers + 1) * 16 * 8;
+  if (bytes < need) return fail(NQ_ERR_INVALID_ARG, "step trace buffer of %lld bytes, need %lld", static_cast<long long>(bytes),
+                                static_cast<long long>(need));
+  if (reinterpret_cast<uintptr_t>(device_buf) % 8 != 0) return fail(NQ_ERR_INVALID_ARG, "step trace buffer not 8-byte aligned");
+  m->step_trace = device_buf;
   return NQ_OK;
 }
 

@@ -681,6 +681,14 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
   int epoch = __builtin_amdgcn_readfirstlane(ld_sc1(p.xflag + x * 64 + li));
   const AttPlan ap = ps_att_plan(pos + 1, p.nkv);
   const int qkv_n = (p.nh + 2 * p.nkv) * D;
+  // optional stage stamps (realtime counter, 100 MHz): row l of this
+  // workgroup holds layer l's 16 events, row L the kernel start, the LM
+  // head's partials and the end of this wave's work
+  auto stamp = [&](int row, int ev) {
+    if (p.stage_trace && lane == 0)
+      p.stage_trace[(static_cast<int64_t>(wg) * (L + 1) + row) * 16 + ev] = __builtin_amdgcn_s_memrealtime();
+  };
+  stamp(L, 0);
 
   // the residual rows of this workgroup's O / down tile (the same tiles: both
   // have N = H) stay in this wave's lanes 0..15 from layer to layer
@@ -735,6 +743,7 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
       }
     }
     ps_barrier();  // QKV partials
+    stamp(l, 0);
     ps_dma_scales(p, s.sca, K_GU, l);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -769,11 +778,14 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
         }
       }
     }
+    stamp(l, 1);
     ps_sync(p, ++epoch, x, li);
+    stamp(l, 2);
     ps_barrier();  // q and this step's K/V are everywhere
 
     // ---- attention: merge the attention waves' partials, then the splits
     ps_barrier();  // attention partials in LDS
+    stamp(l, 3);
     if (wg < p.nkv * ap.S) {
       // this split: the attention waves' partials merged per head (a lane
       // takes columns lane + 64 c of every head; the maxima, sums and weights
@@ -882,20 +894,25 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
       if (g == 0 && o < nout)
         st_h_sc1(hm(p.ao) + o, ps_prescale(static_cast<half_t>(Lt > 0.0f ? Ot / Lt : 0.0f), o % D));
     }
+    stamp(l, 4);
     ps_sync(p, ++epoch, x, li);
+    stamp(l, 5);
     ps_dma(s.xs, hc(p.ao), p.nh * D, true);
     __builtin_amdgcn_s_waitcnt(0);
     ps_barrier();  // O input staged
 
     // ---- O + residual
     ps_barrier();  // O partials
+    stamp(l, 6);
     ps_dma_scales(p, s.scb, K_D, l);
     if (go.nt > 0 && lane < 16) {
       const float y = tile_sum(go, 0, lane);
       hres = static_cast<half_t>(static_cast<float>(hres) + y);
       st_h_sc1(hm(p.hbuf) + go.t0 * 16 + lane, hres);
     }
+    stamp(l, 7);
     ps_sync(p, ++epoch, x, li);
+    stamp(l, 8);
     ps_dma(s.xs, hc(p.hbuf), p.H, true);
     ps_dma(s.gs, hc(Ly.g2), p.H, false);
     __builtin_amdgcn_s_waitcnt(0);
@@ -906,6 +923,7 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
 
     // ---- gate/up + SwiGLU
     ps_barrier();  // gate/up partials
+    stamp(l, 9);
     if (l + 1 < L) ps_dma_scales(p, s.sca, K_QKV, l + 1);
     else ps_dma_scales(p, s.sca, K_LM, l);
     {
@@ -917,13 +935,16 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
         st_h_sc1(hm(p.act) + 8 * (gg.t0 + tl) + rr, ps_prescale(static_cast<half_t>(gv / (1.0f + expf(-gv)) * uv), rr));
       }
     }
+    stamp(l, 10);
     ps_sync(p, ++epoch, x, li);
+    stamp(l, 11);
     ps_dma(s.xs, hc(p.act), p.I, true);
     __builtin_amdgcn_s_waitcnt(0);
     ps_barrier();  // down input staged
 
     // ---- down + residual
     ps_barrier();  // down partials
+    stamp(l, 12);
     if (l + 1 < L) ps_dma_scales(p, s.scb, K_O, l + 1);
     if (gd.nt > 0 && lane < 16) {
       const float y = tile_sum(gd, 0, lane);
@@ -931,19 +952,23 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
       st_h_sc1(hm(p.hbuf) + go.t0 * 16 + lane, hres);
       if (p.layer_out) hm(p.layer_out)[static_cast<int64_t>(l) * p.H + go.t0 * 16 + lane] = hres;
     }
+    stamp(l, 13);
     ps_sync(p, ++epoch, x, li);
+    stamp(l, 14);
     ps_dma(s.xs, hc(p.hbuf), p.H, true);
     ps_dma(s.gs, hc(l + 1 < L ? p.layer[l + 1].g1 : p.gfinal), p.H, false);
     __builtin_amdgcn_s_waitcnt(0);
     ss = ps_stage_gain(s.xs, s.gs, p.H);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     ps_barrier();  // next layer's QKV (or the LM head's) input staged
+    stamp(l, 15);
     rs = ps_rms(ss, p.H, p.eps);
   }
 
   // ---- LM head: fp32 logits, this workgroup's greedy (max, index), and the
   // last workgroup to finish merges all of them
   ps_barrier();  // LM partials
+  stamp(L, 1);
   const Geo gl = ps_geo(p, K_LM, wg, 0);
   float best = -INFINITY;
   int bi = 0x7fffffff;
@@ -1005,6 +1030,7 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
       p.pos[0] = pos + 1;
     }
   }
+  stamp(L, 2);
 }
 
 template <int D, int REP>

@@ -21,8 +21,8 @@ from . import (NQConfig, NQLayerPtrs, NQStepIO, NQ_MAT_PLAIN, NQ_MAT_QKV, NQ_MAT
                nq_rope_table_fill, nq_workspace_bytes, nq_model_bind_workspace, nq_model_destroy,
                nq_kv_pool_bytes, nq_kv_alloc, nq_kv_free, nq_decode_step, nq_graph_capture, nq_graph_launch,
                nq_graph_destroy, nq_graph_kernel_count, nq_check_device_error, NQPrefillIO,
-               nq_prefill_workspace_bytes, nq_prefill, nq_model_set_step_mode, nq_step_kernels, NQ_STEP_AUTO,
-               NQ_STEP_KERNELS)
+               nq_prefill_workspace_bytes, nq_prefill, nq_model_set_step_mode, nq_step_kernels, nq_model_set_step_trace,
+               NQ_STEP_AUTO, NQ_STEP_KERNELS)
 
 STEP_MODES = {"auto": NQ_STEP_AUTO, "kernels": NQ_STEP_KERNELS}
 
@@ -137,6 +137,14 @@ class DeviceModel:
 
     def step_kernels(self, batch: int, max_pages: int) -> int:
         return nq_step_kernels(self.handle, batch, max_pages)
+
+    def set_step_trace(self, buf) -> None:
+        """Stage stamps of the persistent step into ``buf`` (a device tensor of
+        at least 256 * (layers + 1) * 16 int64), or off with None."""
+        if buf is None:
+            nq_model_set_step_trace(self.handle, None, 0)
+        else:
+            nq_model_set_step_trace(self.handle, buf, buf.numel() * buf.element_size())
 
     def weight_bytes(self) -> int:
         n = sum(t.numel() * t.element_size() for t in self._keep)

@@ -15,15 +15,20 @@ the attention sweep (the attention and combine kernels at batch 1 over 511,
 W4A16 GEMV sweep at the 7B projection shapes (GB/s and fraction of the 8 TB/s
 HBM peak; beside each, the INT8-activation variant with its quantisation fused
 into the GEMV and as a separate kernel), the roofline of the dominant kernel
-(the gate/up GEMV + SwiGLU) and the CPU oracle timed on bounded samples.
+(at batch 1 the persistent step kernel, the only kernel of the timed graph),
+the gate/up GEMV + SwiGLU (the largest kernel of the one-kernel-per-stage step)
+and the CPU oracle timed on bounded samples.
 
-Modes (for profiling runs): --mode roofline launches only the gate/up GEMV of
-28 distinct weight copies; --mode copy runs a 1 GiB device copy (the
-calibration for the FETCH_SIZE / WRITE_SIZE counters); --mode stepkern runs a
-few batch-1 steps at context 520 with one kernel per stage and as the
-persistent kernel, then the attention kernels at 4097 and 32767 tokens (for
-per-kernel counters); --mode stagetrace runs the batch-1 configuration's
-persistent step with its stage stamps on and prints the per-stage timeline.
+Modes (for profiling runs): --mode steproof runs only the headline's batch-1
+phase (the prefill, then --warmup and --steps replays of the persistent step);
+--mode roofline launches only the gate/up GEMV of 28 distinct weight copies;
+--mode limits measures the cost of a kernel boundary inside a graph and the
+reuse of weights across consecutive GEMV launches; --mode copy runs a 1 GiB
+device copy (the calibration for the FETCH_SIZE / WRITE_SIZE counters);
+--mode stepkern runs a few batch-1 steps at context 520 with one kernel per
+stage and as the persistent kernel, then the attention sweep (for per-kernel
+counters); --mode stagetrace runs the batch-1 configuration's persistent step
+with its stage stamps on and prints the per-stage timeline.
 """
 from __future__ import annotations
 
@@ -46,6 +51,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_gate_up_swiglu_7b_b1_pmc.md"
 KERNEL_SRC = os.path.join(ROOT, "w4a16_gemv_paged_amd", "csrc", "kernels.hip")
 DEVICE_HDR = os.path.join(ROOT, "w4a16_gemv_paged_amd", "csrc", "device.hpp")
 ATTN_MARK = b"// ============================================================== attention"
+STEP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_7b_b1_persistent_pmc.md")
+STEP_SRCS = [os.path.join(ROOT, "w4a16_gemv_paged_amd", "csrc", n) for n in ("step.hip", "device.hpp", "common.hpp")]
+STEP_KERNEL = "decode_step_kernel<128, 7> (persistent whole step, batch 1)"
 
 
 def log(msg: str) -> None:
@@ -78,16 +86,24 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM traffic per gate/up launch from the committed PMC summary, if it was
-    taken on the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def step_sha() -> str:
+    """Hash of the source the persistent step kernel is built from."""
+    h = hashlib.sha256()
+    for path in STEP_SRCS:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(path: str = TRAFFIC_FILE, sha=kernel_sha):
+    """HBM traffic per launch from a committed PMC summary, if it was taken on
+    the current kernel source."""
+    if not os.path.exists(path):
         return None
-    m = re.search(r"TRAFFIC_JSON:\s*(\{.*\})", open(TRAFFIC_FILE).read())
+    m = re.search(r"TRAFFIC_JSON:\s*(\{.*\})", open(path).read())
     if not m:
         return None
     d = json.loads(m.group(1))
-    if d.get("kernel_sha") != kernel_sha():
+    if d.get("kernel_sha") != sha():
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -514,12 +530,149 @@ def cpu_baseline(shape, head, sample_layers: int = 1, head_frac: int = 8, budget
             "s_per_token": round(per_token, 3), "timed_s": round(timed, 2), "setup_s": round(setup, 1)}
 
 
+def limits(shape, stream, launches: int = 256, replays: int = 8) -> dict:
+    """Fixed costs and cache reuse, measured with the library's own kernels.
+    (1) The per-launch floor: ``launches`` KV appends of one token (one
+    64-thread workgroup writing 4 KiB) captured in one HIP graph and replayed
+    ``replays`` times; the graph time per launch against the kernel's own
+    duration (from a kernel trace of this mode) is the cost of a kernel
+    boundary. (2) Reuse across consecutive launches: the QKV GEMV (8.5 MB, less
+    than the eight 4 MB L2s together) and the gate/up GEMV (70 MB, less than
+    the 256 MB last-level cache) back to back on one copy of the weights,
+    against a rotation over distinct copies (>= 512 MB, nothing reused)."""
+    import numpy as np
+    import torch
+    import synth
+    import w4a16_gemv_paged_amd as nq
+    sid = stream.cuda_stream
+    cfg = nq.NQConfig.from_shape(shape, 1, 4096)
+    npages = 8
+    nbytes = nq.nq_kv_pool_bytes(cfg, npages)
+    pool = torch.zeros(nbytes // 2, dtype=torch.int16, device="cuda")
+    kv = nq.nq_kv_alloc(cfg, pool, nbytes, npages)
+    pt = torch.arange(npages, dtype=torch.int32, device="cuda").view(1, npages)
+    pos = torch.tensor([5], dtype=torch.int32, device="cuda")
+    k = torch.randn(1, shape.n_kv_heads, shape.head_dim, device="cuda").half()
+    v = torch.randn(1, shape.n_kv_heads, shape.head_dim, device="cuda").half()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    append = lambda: nq.nq_kv_append(kv, 0, 1, pt, npages, pos, k, v, err, stream=sid)
+    with torch.cuda.stream(stream):
+        append()
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(launches):
+                append()
+        g.replay()
+        stream.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+        stream.synchronize()
+    nq.nq_check_device_error(err)
+    floor_us = e0.elapsed_time(e1) * 1e3 / (launches * replays)
+    del g
+    nq.nq_kv_free(kv)
+    log(f"kernel floor: {floor_us:.2f} us per graph-launched kernel")
+    reuse = []
+    for (kk, n), copies in (((3584, 4608), 64), ((3584, 37888), 8)):
+        packed = nq.nq_pack_weights(synth.gemv_weight(kk, n, seed=0))
+        bufs = [torch.from_numpy(packed).cuda() for _ in range(copies)]
+        x = torch.from_numpy(synth.activations(1, kk, seed=1).view(np.int16)).cuda()
+        y = torch.empty(1, n, dtype=torch.float16, device="cuda")
+        gemv = lambda j: nq.nq_gemv_w4a16(bufs[j % copies], n, kk, 0, 0, 1, x, None, 1e-6, None, y, 0, sid)
+        with torch.cuda.stream(stream):
+            for j in range(copies):
+                gemv(j)
+            _, rot = time_launches(gemv, copies, stream, reps=max(1, 256 // copies))
+            _, same = time_launches(lambda j: gemv(0), copies, stream, reps=max(1, 256 // copies))
+        nb = gemv_bytes(kk, n, 1)
+        reuse.append({"K": kk, "N": n, "bytes": nb, "distinct_copies_us": round(rot * 1e6, 2),
+                      "same_copy_us": round(same * 1e6, 2), "distinct_GBs": round(nb / rot / 1e9, 1),
+                      "same_GBs": round(nb / same / 1e9, 1)})
+        log(f"GEMV {kk}x{n}: distinct copies {rot * 1e6:.2f} us, same copy {same * 1e6:.2f} us")
+        del bufs
+        torch.cuda.empty_cache()
+    return {"mode": "limits", "graph_launches": launches, "replays": replays,
+            "kv_append_graph_us_per_launch": round(floor_us, 3), "gemv_reuse": reuse}
+
+
+def b1_phase(dm, shape, stream, W: int, K: int, ttft_reps: int = 6) -> dict:
+    """The headline: a 512-token random prompt through the chunked prefill (time
+    to first token, median of ``ttft_reps`` - 1 repeats on the same pages), then
+    the step captured as one HIP graph, W untimed and K timed replays (host clock
+    and HIP events on the replay stream), then 16 eager steps."""
+    import numpy as np
+    import torch
+    import synth
+    from w4a16_gemv_paged_amd.engine import KVCache, Stepper, Prefill
+    P = 512
+    prompt = synth.prompt_ids(P, shape.vocab, seed=2)
+    need = P + W + K + 64
+    max_pages = (need + 15) // 16
+    pt, total = synth.decode_page_tables(1, max_pages, seed=3)
+    kv1 = KVCache(dm, total, poison=False)
+    st = Stepper(dm, kv1, pt, hist_len=need + 1)
+    with torch.cuda.stream(stream):
+        # the prefill leaves the first generated token and its position in the
+        # step's device buffers; the repeats rewrite the same pages
+        pf = Prefill(dm, kv1, P)
+        row = st.page_table[0]
+        ttft = []
+        for r in range(ttft_reps):
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ea.record(stream)
+            pf.run(prompt, row, 0, next_token=st.tokens[0:1], pos_out=st.pos[0:1], stream=stream)
+            eb.record(stream)
+            torch.cuda.synchronize()
+            if r > 0:
+                ttft.append(ea.elapsed_time(eb))
+        pf.check(stream)
+        ttft_ms = float(np.median(ttft))
+        del pf
+        n_kernels = st.capture(stream)
+        log(f"prefill of {P} tokens (TTFT): {ttft_ms:.2f} ms; captured the step: {n_kernels} kernels")
+        for _ in range(W):
+            st.replay(stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t1 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(K):
+            st.replay(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t1
+        st.check(stream)
+        # eager launches of the same step (the pages' eager vs graph comparison)
+        ne = 16
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(ne):
+            st.step(stream)
+        torch.cuda.synchronize()
+        ms_eager = (time.perf_counter() - t2) * 1e3 / ne
+        st.check(stream)
+    gen = st.hist.cpu().numpy()[0][P + 1:P + 1 + W + K]
+    st.close()
+    kv1.close()
+    # the step at position p reads the K/V rows of p + 1 tokens; the timed
+    # replays run at positions P + W .. P + W + K - 1
+    lens = [P + W + i + 1 for i in range(K)]
+    alg = step_weight_bytes(shape) + shape.layers * attn_bytes(shape, lens) / K
+    return {"P": P, "prompt": prompt, "pt": pt, "total": total, "need": need, "ttft_ms": ttft_ms,
+            "n_kernels": n_kernels, "ctx0": P + W, "ms": wall * 1e3 / K, "ms_events": e0.elapsed_time(e1) / K,
+            "ms_eager": ms_eager, "gen": gen, "alg_bytes_per_step": int(round(alg))}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=248)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--mode", choices=["full", "roofline", "copy", "stepkern", "stagetrace"], default="full")
+    ap.add_argument("--mode", choices=["full", "steproof", "limits", "roofline", "copy", "stepkern", "stagetrace"], default="full")
     ap.add_argument("--skip-b8", action="store_true")
     ap.add_argument("--skip-sweep", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
@@ -564,6 +717,10 @@ def main() -> int:
         print(json.dumps({"mode": "roofline", "roofline": r}), flush=True)
         return 0
 
+    if args.mode == "limits":
+        print(json.dumps(limits(shape, stream)), flush=True)
+        return 0
+
     if args.mode == "stagetrace":
         print(json.dumps(stage_trace(shape, stream)), flush=True)
         return 0
@@ -591,6 +748,17 @@ def main() -> int:
         print(json.dumps({"mode": "stepkern", "steps_per_mode": 4, "context": 520, "attention": att}), flush=True)
         return 0
 
+    if args.mode == "steproof":
+        head = synth.head_params(shape, seed=0)
+        dm = DeviceModel(shape, lambda l: synth.layer_params(shape, l, seed=0), head, max_batch=8, max_pos=32768)
+        r1 = b1_phase(dm, shape, stream, args.warmup, args.steps, ttft_reps=1)
+        dm.close()
+        print(json.dumps({"mode": "steproof", "kernel": STEP_KERNEL, "kernel_sha": step_sha(),
+                          "warmup": args.warmup, "steps": args.steps, "context_during_timing":
+                          [r1["ctx0"], r1["ctx0"] + args.steps], "ms_per_token_events": round(r1["ms_events"], 4),
+                          "alg_bytes_per_step": r1["alg_bytes_per_step"]}), flush=True)
+        return 0
+
     # ------------------------------------------------------------------ model
     t0 = time.time()
     log("drawing and packing the 7B-shaped weights")
@@ -600,65 +768,13 @@ def main() -> int:
     log(f"model ready in {time.time() - t0:.1f} s ({dm.weight_bytes() / 1e9:.2f} GB on device)")
 
     # ------------------------------------------------------------------ B = 1
-    P = 512
     W, K = args.warmup, args.steps
-    prompt = synth.prompt_ids(P, shape.vocab, seed=2)
-    need = P + W + K + 64
-    max_pages = (need + 15) // 16
-    pt, total = synth.decode_page_tables(1, max_pages, seed=3)
-    kv1 = KVCache(dm, total, poison=False)
-    st = Stepper(dm, kv1, pt, hist_len=need + 1)
-    with torch.cuda.stream(stream):
-        # time to first token: the prompt through the chunked prefill (one chunk of
-        # P rows), which leaves the first generated token and its position in the
-        # step's device buffers; timed over a few repeats on the same pages
-        pf = Prefill(dm, kv1, P)
-        row = st.page_table[0]
-        ttft = []
-        for r in range(6):
-            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            ea.record(stream)
-            pf.run(prompt, row, 0, next_token=st.tokens[0:1], pos_out=st.pos[0:1], stream=stream)
-            eb.record(stream)
-            torch.cuda.synchronize()
-            if r > 0:
-                ttft.append(ea.elapsed_time(eb))
-        pf.check(stream)
-        ttft_ms = float(np.median(ttft))
-        del pf
-        n_kernels = st.capture(stream)
-        log(f"prefill of {P} tokens (TTFT): {ttft_ms:.2f} ms; captured the step: {n_kernels} kernels")
-        for _ in range(W):
-            st.replay(stream)
-        torch.cuda.synchronize()
-        ctx0 = P + W
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t1 = time.perf_counter()
-        e0.record(stream)
-        for _ in range(K):
-            st.replay(stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t1
-        ms_b1 = wall * 1e3 / K
-        ms_b1_events = e0.elapsed_time(e1) / K
-        st.check(stream)
-        # eager launches of the same step (the pages' eager vs graph comparison)
-        ne = 16
-        torch.cuda.synchronize()
-        t2 = time.perf_counter()
-        for _ in range(ne):
-            st.step(stream)
-        torch.cuda.synchronize()
-        ms_eager = (time.perf_counter() - t2) * 1e3 / ne
-        st.check(stream)
-    hist = st.hist.cpu().numpy()[0]
-    gen = hist[P + 1:P + 1 + W + K]
+    r1 = b1_phase(dm, shape, stream, W, K)
+    P, prompt, pt, total, need = r1["P"], r1["prompt"], r1["pt"], r1["total"], r1["need"]
+    ms_b1, ms_b1_events, ms_eager, ttft_ms, n_kernels, ctx0, gen = (
+        r1["ms"], r1["ms_events"], r1["ms_eager"], r1["ttft_ms"], r1["n_kernels"], r1["ctx0"], r1["gen"])
     log(f"B=1: {ms_b1:.3f} ms/token ({1e3 / ms_b1:.1f} tok/s), eager {ms_eager:.3f} ms/token; "
         f"first tokens {gen[:8].tolist()}")
-    st.close()
-    kv1.close()
-    del st, kv1
     # the same prompt, page table and timed contexts with one kernel per stage
     dm.set_step_mode("kernels")
     kv1 = KVCache(dm, total, poison=False)
@@ -692,6 +808,18 @@ def main() -> int:
     del st, kv1
 
     # ------------------------------------------------------------------ roofline of the dominant kernel
+    # At batch 1 the timed graph holds one kernel, the persistent step, so its
+    # average launch duration is the replay time measured by the HIP events on
+    # the replay stream, and its algorithmic bytes are the step's weights plus
+    # every layer's K/V rows at the timed contexts.
+    alg = r1["alg_bytes_per_step"]
+    roof_step = {"kernel": STEP_KERNEL, "bound": "hbm",
+                 "achieved": round(alg / (ms_b1_events * 1e-3) / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
+                 "frac": round(alg / (ms_b1_events * 1e-3) / PEAK_HBM, 4),
+                 "traffic": read_traffic(STEP_TRAFFIC_FILE, step_sha),
+                 "algorithmic_bytes_per_launch": alg, "mean_launch_us": round(ms_b1_events * 1e3, 2),
+                 "launches_timed": K}
+    log(f"persistent step kernel: {roof_step['achieved']} GB/s ({roof_step['frac'] * 100:.1f}% of 8 TB/s)")
     with torch.cuda.stream(stream):
         roof = gate_up_roofline([(L["gate_up"], L["g2"]) for L in dm.layers], shape.hidden, shape.intermediate,
                                 stream, reps=10)
@@ -768,9 +896,10 @@ def main() -> int:
                                "step replayed as one HIP graph", "batch": 1, "prompt_tokens": P,
                    "context_during_timing": [ctx0, ctx0 + K], "weights": "int4 symmetric g128, fp16 scales",
                    "activations": "fp16, fp32 accumulation", "kernels_per_step": n_kernels},
-        "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
-        "traffic_source": ("profiles/gemv_gate_up_swiglu_7b_b1_pmc.md: rocprofv3 FETCH_SIZE / WRITE_SIZE runs on "
-                           "the same GEMV source hash (not measured in this run; null when the hash differs)"),
+        "roofline": {k: roof_step[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "traffic_source": ("profiles/decode_step_7b_b1_persistent_pmc.md: rocprofv3 FETCH_SIZE / WRITE_SIZE runs "
+                           "of bench.py --mode steproof on the same step source hash (not measured in this run; "
+                           "null when the hash differs)"),
         "cpu_baseline": cpu,
         "ms_per_token_b1_events": round(ms_b1_events, 4),
         "ms_per_token_b1_eager": round(ms_eager, 4),
@@ -780,7 +909,8 @@ def main() -> int:
         "step_weight_bytes": wb,
         "step_roofline_ms": round(wb / PEAK_HBM * 1e3, 4),
         "step_roofline_frac": round(wb / PEAK_HBM * 1e3 / ms_b1, 4),
-        "dominant_kernel": roof,
+        "dominant_kernel": roof_step,
+        "gemv_gate_up_roofline": roof,
         "ttft": ttft_block(shape, P, ttft_ms, ms_b1),
         "b8": b8,
         "gemv_sweep": sweep, "gemv_aggregate": agg,

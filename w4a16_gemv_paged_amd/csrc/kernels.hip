@@ -96,6 +96,43 @@ __device__ __forceinline__ f4 gemv_block_mfma(const u32x4& w, const half_t* xg, 
   return d;
 }
 
+// The RMSNorm prologue over the staged rows: x * gain in place, pre-scaled for
+// the biased codes (fp16 products, as the GEMV forms them), and each wave's
+// partial sum of x^2 per batch row (1/rms multiplies the outputs later).
+// Thread t takes row t % BP (B rounded up to a power of two; threads of rows
+// >= B stay idle) and every (blockDim / BP)-th 16-byte item of it, so a
+// wave's partial sums of row b sit in the lanes congruent to b mod BP and
+// log2(64 / BP) shuffle steps reduce every row at once. Returns, in lane b <
+// B, the wave's sum for row b. h_out (if set) receives the rows as staged.
+template <int B>
+__device__ __forceinline__ float gain_rows(half_t* xs, int xrow, const half_t* gs, int n8, half_t* h_out,
+                                           int64_t K, int64_t k0) {
+  constexpr int BP = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8;
+  static_assert(B <= 8, "batch rows");
+  const int tid = threadIdx.x;
+  const int b = tid % BP;
+  const h2 sixteenth = {static_cast<half_t>(0.0625f), static_cast<half_t>(0.0625f)};
+  float s = 0.0f;
+  if (b < B) {
+    for (int j = tid / BP; j < n8; j += blockDim.x / BP) {
+      uint4 v = *reinterpret_cast<const uint4*>(xs + b * xrow + j * 8);
+      const uint4 gv = *reinterpret_cast<const uint4*>(gs + j * 8);
+      if (h_out) *reinterpret_cast<uint4*>(h_out + b * K + k0 + j * 8) = v;
+      h2* x = reinterpret_cast<h2*>(&v);
+      const h2* g = reinterpret_cast<const h2*>(&gv);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s = __builtin_amdgcn_fdot2(x[q], x[q], s, false);
+      x[0] = x[0] * g[0];
+      x[1] = (x[1] * g[1]) * sixteenth;
+      x[2] = x[2] * g[2];
+      x[3] = (x[3] * g[3]) * sixteenth;
+      *reinterpret_cast<uint4*>(xs + b * xrow + j * 8) = v;
+    }
+  }
+  for (int o = 32; o >= BP; o >>= 1) s += __shfl_xor(s, o);
+  return s;
+}
+
 template <int B, int EPI, bool GAIN>
 __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -188,9 +225,7 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
 
   u32x4 wv[kDepth];
   f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  float ss[B];
-#pragma unroll
-  for (int b = 0; b < B; ++b) ss[b] = 0.0f;
+  float ss = 0.0f;  // lane b < B: this wave's sum of x^2 of row b over the chunks so far
 
   auto chunk = [&](const int c0) {
     const int c1 = min(p.G, c0 + p.ch);
@@ -257,26 +292,7 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
     //     (1/rms multiplies the outputs later); workgroup 0 also stores the
     //     gathered embedding rows as the residual
     if constexpr (GAIN) {
-      for (int i = tid; i < B * n8; i += blockDim.x) {
-        const int b = i / n8, j = i - b * n8;
-        uint4 v = *reinterpret_cast<const uint4*>(xs + b * xrow + j * 8);
-        const uint4 gv = *reinterpret_cast<const uint4*>(gs + j * 8);
-        if (p.h_out && blockIdx.x == 0)
-          *reinterpret_cast<uint4*>(p.h_out + static_cast<int64_t>(b) * p.K + static_cast<int64_t>(c0) * 128 + j * 8) = v;
-        half_t* hv = reinterpret_cast<half_t*>(&v);
-        const half_t* gh = reinterpret_cast<const half_t*>(&gv);
-        float sacc = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float f = static_cast<float>(hv[e]);
-          sacc = fmaf(f, f, sacc);
-          hv[e] = static_cast<half_t>(f * static_cast<float>(gh[e]) * high_scale(e));
-        }
-#pragma unroll
-        for (int bb = 0; bb < B; ++bb)
-          if (bb == b) ss[bb] += sacc;
-        *reinterpret_cast<uint4*>(xs + b * xrow + j * 8) = v;
-      }
+      ss += gain_rows<B>(xs, xrow, gs, n8, blockIdx.x == 0 ? p.h_out : nullptr, p.K, static_cast<int64_t>(c0) * 128);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
@@ -313,12 +329,7 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
 
   // per-wave partial sums of x^2, and the tile rows of this wave
   if constexpr (GAIN) {
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      float v = ss[b];
-      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-      if (lane == 0) ssq[wave * B + b] = v;
-    }
+    if (lane < B) ssq[wave * B + lane] = ss;
   }
   __syncthreads();  // every wave is done reading xs; red is free
   if (col < B) {
@@ -626,25 +637,8 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvPara
   // (3) x * gain in place, pre-scaled for the biased codes, and each wave's
   //     share of sum(x^2) per batch row
   if constexpr (GAIN) {
-    const int n8 = G * 16;
-    for (int b = 0; b < B; ++b) {
-      float sacc = 0.0f;
-      for (int j = tid; j < n8; j += blockDim.x) {
-        uint4 v = *reinterpret_cast<const uint4*>(xs + b * xrow + j * 8);
-        const uint4 gv = *reinterpret_cast<const uint4*>(gs + j * 8);
-        half_t* hv = reinterpret_cast<half_t*>(&v);
-        const half_t* gh = reinterpret_cast<const half_t*>(&gv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float f = static_cast<float>(hv[e]);
-          sacc = fmaf(f, f, sacc);
-          hv[e] = static_cast<half_t>(f * static_cast<float>(gh[e]) * high_scale(e));
-        }
-        *reinterpret_cast<uint4*>(xs + b * xrow + j * 8) = v;
-      }
-      for (int o = 32; o >= 1; o >>= 1) sacc += __shfl_xor(sacc, o);
-      if (lane == 0) ssq[wave * B + b] = sacc;
-    }
+    const float sw = gain_rows<B>(xs, xrow, gs, G * 16, nullptr, 0, 0);
+    if (lane < B) ssq[wave * B + lane] = sw;
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);

@@ -36,10 +36,13 @@ namespace nq {
 // summed through LDS, then the fused epilogue runs on (tile, batch, row) items.
 
 constexpr int kDepth = 7;                   // 1 KiB weight loads in flight per wave
-constexpr int kDmaBatch = 8;                // activation copies issued back to back per wave
 constexpr int kGemvCUs = 256;               // MI355X compute units: one workgroup each in an even spread
 constexpr size_t kLdsMax = 160 * 1024;      // LDS of a workgroup on gfx950
 constexpr size_t kLdsX = 152 * 1024;        // LDS budget for staged activations and gain
+// Staged rows of a batch > 1 are padded by 16 bytes, so that the rows' items at
+// the same K start in different LDS banks: the matrix-core reads of the batch
+// columns and the RMSNorm pass read one K offset of every row at once.
+constexpr int kRowPad = 8;
 
 struct GemvParams {
   const uint8_t* codes;
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
                        : min(p.T, t0 + p.tpw);
   const int t = t0 + tl;
   const bool tile_ok = t < t1;  // wave-uniform
-  const int xrow = p.xrow;       // halfs per staged row, a multiple of 512 (1 KiB)
+  const int xrow = p.xrow;       // halfs per staged row: a multiple of 512 (1 KiB), padded at batch > 1
   // LDS: [B] activation rows | gain row (GAIN) | zero block | red | ssq | lg
   half_t* xs = reinterpret_cast<half_t*>(smem);
   half_t* gs = xs + B * xrow;
@@ -236,33 +239,28 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
     // (1) Activations (and gain) straight into LDS, one 1 KiB block per wave
     //     instruction, issued before the weights: the memory counter retires
     //     in order, so they can be waited for without waiting for the weights.
-    const int nblk = (B + (GAIN ? 1 : 0)) * rblk;
-    const int mine = (nblk - wave + nw - 1) / nw;  // blocks of this wave
-    for (int r0 = 0; r0 < mine; r0 += kDmaBatch) {
-      // straight-line batches: the copies go out back to back
-#pragma unroll
-      for (int q = 0; q < kDmaBatch; ++q) {
-        const int bi = wave + (r0 + q) * nw;
-        if (r0 + q < mine) {
-          const int r = bi / rblk, j = bi - r * rblk;
-          const int item = j * 64 + lane;
-          const half_t* src;
-          half_t* dst;
-          if (r < B) {
-            const half_t* xr = p.x + static_cast<int64_t>(r) * p.K;
-            if (p.embed) {  // activation row r is the embedding row of the input token
-              int tok = __builtin_amdgcn_readlane(tok_lane, r);
-              if (tok < 0 || tok >= p.vocab) tok = 0;
-              xr = p.embed + static_cast<int64_t>(tok) * p.K;
-            }
-            src = xr + static_cast<int64_t>(c0) * 128 + item * 8;
-            dst = xs + r * xrow + j * 512;
-          } else {
-            src = p.gain + static_cast<int64_t>(c0) * 128 + item * 8;
-            dst = gs + j * 512;
-          }
-          if (item < n8) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    //     Block j of every row goes to wave j mod nw; the row loop keeps the
+    //     per-copy address work to increments.
+#pragma unroll 1
+    for (int r = 0; r < B + (GAIN ? 1 : 0); ++r) {
+      const half_t* src;
+      half_t* dst;
+      if (r < B) {
+        const half_t* xr = p.x + static_cast<int64_t>(r) * p.K;
+        if (p.embed) {  // activation row r is the embedding row of the input token
+          int tok = __builtin_amdgcn_readlane(tok_lane, r);
+          if (tok < 0 || tok >= p.vocab) tok = 0;
+          xr = p.embed + static_cast<int64_t>(tok) * p.K;
         }
+        src = xr + static_cast<int64_t>(c0) * 128;
+        dst = xs + r * xrow;
+      } else {
+        src = p.gain + static_cast<int64_t>(c0) * 128;
+        dst = gs;
+      }
+      for (int j = wave; j < rblk; j += nw) {
+        const int item = j * 64 + lane;
+        if (item < n8) __builtin_amdgcn_global_load_lds(src + item * 8, dst + j * 512, 16, 0, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -493,7 +491,7 @@ static StreamPlan stream_plan(int T, int G, int B, bool gain) {
   StreamPlan s;
   s.tiles_per_group = (T + kStreamGroups - 1) / kStreamGroups;
   s.chunks_per_tile = (G + kStreamChunk - 1) / kStreamChunk;
-  s.xrow = (G * 128 + 511) / 512 * 512;
+  s.xrow = (G * 128 + 511) / 512 * 512 + (B > 1 ? kRowPad : 0);
   const int rows = B + (gain ? 1 : 0);
   const size_t xbytes = static_cast<size_t>(rows) * s.xrow * 2;
   const size_t lg = static_cast<size_t>(s.tiles_per_group) * B * 16 * 4;  // argmax logits, reuse the x rows
@@ -558,19 +556,13 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvPara
   {
     const int n8 = G * 16;                  // 16-byte items per row
     const int rblk = (n8 + 63) / 64;        // 1 KiB blocks per row
-    const int nblk = (B + (GAIN ? 1 : 0)) * rblk;
-    const int mine = (nblk - wave + NW - 1) / NW;
-    for (int r0 = 0; r0 < mine; r0 += kDmaBatch) {
-#pragma unroll
-      for (int q = 0; q < kDmaBatch; ++q) {
-        const int bi = wave + (r0 + q) * NW;
-        if (r0 + q < mine) {
-          const int r = bi / rblk, j = bi - r * rblk;
-          const int item = j * 64 + lane;
-          const half_t* src = r < B ? p.x + static_cast<int64_t>(r) * p.K + item * 8 : p.gain + item * 8;
-          half_t* dst = r < B ? xs + r * xrow + j * 512 : gs + j * 512;
-          if (item < n8) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-        }
+#pragma unroll 1
+    for (int r = 0; r < B + (GAIN ? 1 : 0); ++r) {  // block j of every row on wave j mod NW
+      const half_t* src = r < B ? p.x + static_cast<int64_t>(r) * p.K : p.gain;
+      half_t* dst = r < B ? xs + r * xrow : gs;
+      for (int j = wave; j < rblk; j += NW) {
+        const int item = j * 64 + lane;
+        if (item < n8) __builtin_amdgcn_global_load_lds(src + item * 8, dst + j * 512, 16, 0, 0);
       }
     }
   }
@@ -791,7 +783,7 @@ static GemvShape gemv_shape(int T, int G, int B, bool gain) {
   // multiple of them: at batch 8 the down projection's 148 groups take two
   // chunks of 76 and 72 (19.3 us) instead of three of 64, 64 and 20 (20.7 us)
   s.ch = G <= fit ? G : std::max(4, fit);
-  s.xrow = (s.ch * 128 + 511) / 512 * 512;
+  s.xrow = (s.ch * 128 + 511) / 512 * 512 + (B > 1 ? kRowPad : 0);
   s.threads = s.tpw * s.ks * 64;
   if (!s.bal) s.grid = (T + s.tpw - 1) / s.tpw;
   s.lds = static_cast<size_t>(rows) * s.xrow * 2 + extras;

@@ -8,12 +8,13 @@ prompt fed through the chunked prefill (timed: the time to first token), then
 the step replayed as one HIP graph per token; ``value`` = tokens/s over exactly
 --steps timed replays (after --warmup). At batch 1 the step is the persistent
 whole-step kernel; the same tokens are then timed with one kernel per stage.
-The same line also carries batch 1 at contexts 4097 and 32767 in both step
-modes, the batch-8 decode (ragged contexts uniform in [128, 16384], 128 steps),
+The same line also carries the persistent step's per-stage GEMV rates from its
+own stage stamps (16 replays with the stamps on), batch 1 at contexts 4097 and
+32767 in both step modes, the batch-8 decode (ragged contexts uniform in [128, 16384], 128 steps),
 the attention sweep (the attention and combine kernels at batch 1 over 511,
 4097 and 32767 tokens and at batch 8 over ragged lengths in [1, 32767]), the
-W4A16 GEMV sweep at the 7B projection shapes (GB/s and fraction of the 8 TB/s
-HBM peak; beside each, the INT8-activation variant with its quantisation fused
+W4A16 GEMV sweep at the 7B projection shapes (timed as graph replays: GB/s and
+fraction of the 8 TB/s HBM peak; beside each, the INT8-activation variant with its quantisation fused
 into the GEMV and as a separate kernel), the roofline of the dominant kernel
 (at batch 1 the persistent step kernel, the only kernel of the timed graph),
 the gate/up GEMV + SwiGLU (the largest kernel of the one-kernel-per-stage step)
@@ -134,6 +135,28 @@ def time_launches(fn, launches: int, stream, reps: int = 1):
     return sum(per) / len(per), e0.elapsed_time(e1) * 1e-3 / (launches * reps)
 
 
+def time_graph(fn, launches: int, stream, reps: int = 1) -> float:
+    """Seconds per launch of ``reps`` x ``launches`` calls captured in one HIP
+    graph and replayed twice (HIP events on ``stream``): the kernels' own
+    time, without the host's per-call overhead."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(reps):
+            for j in range(launches):
+                fn(j)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e-3 / (2 * reps * launches)
+
+
 PEAK_MFMA_F16 = 2.5e15   # MI355X dense fp16 matrix peak
 
 
@@ -204,11 +227,12 @@ def gemv_sweep(stream):
             fn = lambda j: nq.nq_gemv_w4a16(bufs[j], n, k, 0, 0, b, x, None, 1e-6, None, y, 0, sid)
             for j in range(copies):
                 fn(j)
-            mean_s, b2b_s = time_launches(fn, copies, stream, reps=max(1, 256 // copies))
+            mean_s, eager_s = time_launches(fn, copies, stream, reps=max(1, 256 // copies))
+            b2b_s = time_graph(fn, copies, stream, reps=max(1, 256 // copies))
             nb = gemv_bytes(k, n, b)
             row = {"K": k, "N": n, "B": b, "bytes": nb, "us": round(b2b_s * 1e6, 2),
                    "GBs": round(nb / b2b_s / 1e9, 1), "frac": round(nb / b2b_s / PEAK_HBM, 4),
-                   "event_pair_us": round(mean_s * 1e6, 2)}
+                   "eager_us": round(eager_s * 1e6, 2), "event_pair_us": round(mean_s * 1e6, 2)}
             # the INT8-activation variant on the same weights: a separate quantise
             # kernel before each GEMV, and quantisation in the GEMV prologue
             xq = torch.empty(nq.nq_a8_bytes(b, k), dtype=torch.uint8, device="cuda")
@@ -341,18 +365,29 @@ STAGE_EVENTS = ["QKV partials in", "QKV hand-off: arrive", "QKV hand-off: all ar
                 "next stage's input staged"]
 
 
-def stage_trace(shape, stream, steps: int = 16):
+# (stage, event that starts it: the hand-off before it; None = the previous
+# layer's last hand-off, event that ends it: its partial sums in LDS)
+GEMV_STAGES = [("QKV", None, 0, "qkv"), ("O", 5, 6, "o"), ("gate/up", 8, 9, "gate_up"), ("down", 11, 12, "down")]
+
+
+def stage_trace(shape, stream, steps: int = 16, dm=None):
     """The batch-1 configuration (512-token prompt through the prefill, 52-page
     table) stepped with the persistent kernel's stage stamps on: per event, the
     time since the layer's start (the previous layer's last event), median
     over steps and layers 1..L-2 of the median and of the maximum over the 256
-    workgroups; the layer, LM head and whole-step durations."""
+    workgroups; the layer, LM head and whole-step durations. Per GEMV stage:
+    from the first workgroup's start of the stage (the hand-off before it) to
+    the last workgroup's partial sums in LDS, which takes in the stage's input
+    staging and its weight stream, median over steps and layers; its bytes
+    and rate."""
     import numpy as np
     import torch
     import synth
     from w4a16_gemv_paged_amd.engine import DeviceModel, KVCache, Stepper, Prefill
-    head = synth.head_params(shape, seed=0)
-    dm = DeviceModel(shape, lambda l: synth.layer_params(shape, l, seed=0), head, max_batch=8, max_pos=32768)
+    own = dm is None
+    if own:
+        head = synth.head_params(shape, seed=0)
+        dm = DeviceModel(shape, lambda l: synth.layer_params(shape, l, seed=0), head, max_batch=8, max_pos=32768)
     P, L = 512, shape.layers
     pt, total = synth.decode_page_tables(1, 52, seed=3)
     kv = KVCache(dm, total, poison=False)
@@ -375,8 +410,10 @@ def stage_trace(shape, stream, steps: int = 16):
         dm.set_step_trace(None)
     st.close()
     kv.close()
-    dm.close()
+    if own:
+        dm.close()
     ev_med = [[] for _ in range(16)]
+    span = {name: [] for name, _, _, _ in GEMV_STAGES}
     ev_max = [[] for _ in range(16)]
     layer_us, lm_us, step_us = [], [], []
     for t in samples:
@@ -388,10 +425,24 @@ def stage_trace(shape, stream, steps: int = 16):
                 ev_med[e].append(float(np.median(d)))
                 ev_max[e].append(float(np.max(d)))
             layer_us.append(float(np.median(t[:, l, 15] - t[:, l - 1, 15])))
+            for name, e0, e1, _ in GEMV_STAGES:
+                t0 = t[:, l - 1, 14] if e0 is None else t[:, l, e0]
+                span[name].append(float(np.max(t[:, l, e1]) - np.min(t0)))
         lm_us.append(float(np.median(t[:, L, 2] - t[:, L - 1, 15])))
         step_us.append(float(np.max(t[:, L, 2]) - np.min(t[:, L, 0])))
     med = lambda v: round(float(np.median(v)), 2)
-    return {"mode": "stagetrace", "steps": len(samples), "context": [P + 4, P + 4 + len(samples)],
+    H, I, nh, nkv, d = shape.hidden, shape.intermediate, shape.n_heads, shape.n_kv_heads, shape.head_dim
+    kn = {"qkv": (H, (nh + 2 * nkv) * d), "o": (nh * d, H), "gate_up": (H, 2 * I), "down": (I, H)}
+    stages = []
+    for name, _, _, key in GEMV_STAGES:
+        k, n = kn[key]
+        nb, us = gemv_bytes(k, n, 1), med(span[name])
+        stages.append({"stage": name, "K": k, "N": n, "bytes": nb, "us": us, "GBs": round(nb / us / 1e3, 1),
+                       "frac": round(nb / us / 8e6, 4)})
+    tb, tt = sum(x["bytes"] for x in stages), sum(x["us"] for x in stages)
+    return {"mode": "stagetrace",
+            "gemv_stages": stages,
+            "gemv_stages_aggregate": {"GBs": round(tb / tt / 1e3, 1), "frac": round(tb / tt / 8e6, 4)}, "steps": len(samples), "context": [P + 4, P + 4 + len(samples)],
             "events": [{"event": STAGE_EVENTS[e], "us_since_layer_start_median_wg": med(ev_med[e]),
                         "us_since_layer_start_slowest_wg": med(ev_max[e])} for e in range(16)],
             "layer_us": med(layer_us), "lm_head_and_greedy_us": med(lm_us), "step_us": med(step_us),
@@ -806,6 +857,11 @@ def main() -> int:
     st.close()
     kv1.close()
     del st, kv1
+    # the persistent step's own stage stamps: per-stage GEMV rates in the product path
+    stg = stage_trace(shape, stream, steps=16, dm=dm)
+    log(f"persistent step stages: layer {stg['layer_us']} us; GEMV stages " +
+        ", ".join(f"{x['stage']} {x['us']} us ({x['frac'] * 100:.0f}%)" for x in stg["gemv_stages"]) +
+        f"; aggregate {stg['gemv_stages_aggregate']['frac'] * 100:.1f}% of 8 TB/s")
 
     # ------------------------------------------------------------------ roofline of the dominant kernel
     # At batch 1 the timed graph holds one kernel, the persistent step, so its
@@ -904,6 +960,8 @@ def main() -> int:
         "ms_per_token_b1_events": round(ms_b1_events, 4),
         "ms_per_token_b1_eager": round(ms_eager, 4),
         "b1_kernel_per_stage": b1_kernels,
+        "b1_persistent_stages": {k: stg[k] for k in ("gemv_stages", "gemv_stages_aggregate", "layer_us",
+                                                     "lm_head_and_greedy_us", "step_us", "context")},
         "b1_context_sweep": ctx_sweep,
         "attention_sweep": att_sweep,
         "step_weight_bytes": wb,

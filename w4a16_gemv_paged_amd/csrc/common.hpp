@@ -182,7 +182,7 @@ struct PsParams {
   float eps;
   // workspace: hand-off flags, counters and buffers
   int* xflag;                       // [8][64] per-workgroup epochs, one row per XCD
-  int* xcdflag;                     // [8][16] per-XCD epochs
+  int* xcdflag;                     // [8 reading XCDs][8 XCDs][16] per-XCD epochs, a line each
   int* cnt;                         // [16][16] row 14: per-XCD slot tickets; row 15: LM head
   int* abort;
   uint16_t* hbuf;                   // [H] residual stream

@@ -82,7 +82,7 @@ Workspace carve(const nq_config& c, int32_t batch, int32_t max_pages, uint8_t* b
   };
   const int32_t qd = c.n_heads * c.head_dim;
   w.xflag = reinterpret_cast<int*>(take(static_cast<size_t>(kPsXcds) * 64 * 4));
-  w.xcdflag = reinterpret_cast<int*>(take(static_cast<size_t>(kPsXcds) * 16 * 4));
+  w.xcdflag = reinterpret_cast<int*>(take(static_cast<size_t>(kPsXcds) * kPsXcds * 16 * 4));
   w.cnt = reinterpret_cast<int*>(take(16 * 16 * 4));
   w.abort = reinterpret_cast<int*>(take(256));
   w.ps_h = take(static_cast<size_t>(c.hidden) * 2);

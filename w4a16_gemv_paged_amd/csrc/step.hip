@@ -194,11 +194,13 @@ __device__ void ps_sync(const PsParams& p, int target, int x, int li) {
     __builtin_amdgcn_s_sleep(1);
   }
   if (ok) {
-    if (li == 0 && lane == 0) st_sc1(p.xcdflag + x * 16, target);
+    // the XCD's arrival, one copy (cache line) per reading XCD: an XCD's 32
+    // workgroups poll their own row, so no line has more than 32 pollers
+    if (li == 0 && lane < kPsXcds) st_sc1(p.xcdflag + (lane * kPsXcds + x) * 16, target);
     ok = false;
     for (int it = 0; it < p.max_polls; ++it) {
       bool mine = true;
-      if (lane < kPsXcds) mine = (ld_sc1(p.xcdflag + lane * 16) - target) >= 0;
+      if (lane < kPsXcds) mine = (ld_sc1(p.xcdflag + (x * kPsXcds + lane) * 16) - target) >= 0;
       if (__all(mine)) {
         ok = true;
         break;

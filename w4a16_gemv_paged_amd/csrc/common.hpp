@@ -160,7 +160,7 @@ struct PsLayer {
 struct PsParams {
   PsLayer layer[kPsMaxLayers];
   int L, H, I, nh, nkv, hd, V;
-  int kmax, maxu;                   // longest staged row; most (tile, segment) units per workgroup
+  int kmax, maxu;                   // longest staged row; most (tile, segment) slots per workgroup, segments padded to 4
   int sc_a, sc_b;                   // LDS bytes of the scale buffers (QKV / gate-up / LM; O / down)
   const uint16_t* embed;
   const uint16_t* gfinal;

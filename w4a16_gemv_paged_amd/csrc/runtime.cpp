@@ -185,7 +185,7 @@ int enqueue_step_persistent(nq_model* m, nq_kv* kv, const nq_step_io* io, hipStr
   for (int k = 0; k < 5; ++k) {
     const int64_t tiles = (tiles_of(static_cast<int32_t>(shapes[k][0])) + kPsWG - 1) / kPsWG;
     const int64_t segs = (shapes[k][1] / kGroup + kPsSegGroups - 1) / kPsSegGroups;
-    maxu = std::max(maxu, tiles * segs);
+    maxu = std::max(maxu, tiles * ((segs + 3) / 4 * 4));  // segments of a tile row padded to 4
     sc[k] = tiles * (shapes[k][1] / kGroup) * 32;  // a workgroup's group scales
   }
   p.maxu = static_cast<int>(maxu);

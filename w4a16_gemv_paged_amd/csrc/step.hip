@@ -143,7 +143,7 @@ __device__ __forceinline__ const uint8_t* ps_matrix(const PsParams& p, int layer
 __device__ __forceinline__ int ps_stage_kind(int st, int L) { return st >= 5 * L ? K_LM : st % 5; }
 __device__ __forceinline__ int ps_stage_layer(int st, int L) { return st >= 5 * L ? L - 1 : st / 5; }
 
-// LDS layout (bytes): xs [kmax] fp16 | gs [H] fp16 | part [maxu units][16] f32 |
+// LDS layout (bytes): xs [kmax] fp16 | gs [H] fp16 | part [tiles][16 rows][segments, padded to 4] f32 |
 // att_m [kPsAtt][16] | att_l [kPsAtt][16] | att_o [kPsAtt][16][hd + 4] | geo |
 // sca [sc_a] | scb [sc_b]
 struct PsLds {
@@ -396,7 +396,7 @@ __device__ __forceinline__ void ps_streaming(const PsParams& p, const PsLds& s, 
   // Compute cursor: stage, units left, (tile, segment) of the next unit, the
   // stage's group scales in LDS (staged by the control wave).
   bool done = false;
-  int cst = 0, cleft = 0, cG = 1, cnseg = 1, ctl = 0, cseg = 0;
+  int cst = 0, cleft = 0, cG = 1, cnseg = 1, ctl = 0, cseg = 0, csp = 4;
   const uint8_t* csc = s.sca;
   auto enter_stage = [&](int st) {
     const int kind = ps_stage_kind(st, L);
@@ -404,6 +404,7 @@ __device__ __forceinline__ void ps_streaming(const PsParams& p, const PsLds& s, 
     const int u0 = field(kind, 1);
     cG = field(kind, 2);
     cnseg = field(kind, 3);
+    csp = (cnseg + 3) & ~3;
     ctl = u0 / cnseg;
     cseg = u0 - ctl * cnseg;
     csc = (kind == K_O || kind == K_D) ? s.scb : s.sca;
@@ -443,10 +444,10 @@ __device__ __forceinline__ void ps_streaming(const PsParams& p, const PsLds& s, 
       if (len > 1) blk(w1, 1);
       if (len > 2) blk(w2, 2);
     }
-    if ((lane & 15) == 0) {
-      float* dst = s.part + (ctl * cnseg + cseg) * 16 + 4 * kb;
+    if ((lane & 15) == 0) {  // row-major partials: a tile row's segments are contiguous
+      float* dst = s.part + (ctl * 16 + 4 * kb) * csp + cseg;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = acc[i];
+      for (int i = 0; i < 4; ++i) dst[i * csp] = acc[i];
     }
   };
   ps_barrier();  // the first stage's input is staged
@@ -713,8 +714,15 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
 
   // a tile row: its segments' sums, added in segment order
   auto tile_sum = [&](const Geo& g0, int tl, int rr) {
+    const int sp = (g0.nseg + 3) & ~3;
+    const float* r = s.part + (tl * 16 + rr) * sp;
     float v = 0.0f;
-    for (int sg = 0; sg < g0.nseg; ++sg) v += s.part[(tl * g0.nseg + sg) * 16 + rr];
+    for (int q = 0; q < sp; q += 4) {
+      const f4 c = *reinterpret_cast<const f4*>(r + q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (q + e < g0.nseg) v += c[e];
+    }
     return v;
   };
 

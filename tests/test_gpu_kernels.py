@@ -156,6 +156,26 @@ def test_gemv_norm_gain_multi_chunk(batch):
     assert rel_inf(host(y), oracle.gemv_w4a16(qo, so, xh, b).astype(F16)) < TOL_LAYER
 
 
+@pytest.mark.parametrize("batch", [2, 3, 5, 6, 7])
+def test_gemv_norm_prologue_odd_batches(batch):
+    """The RMSNorm prologue at batch sizes that are not a power of two: the pass
+    gives each thread one batch row (the row count rounded up to a power of two,
+    the threads of the extra rows idle) and reduces every row's sum of squares
+    at once. Checked in the per-tile GEMV and in the streaming GEMV (at least 16
+    row tiles per workgroup, the LM head's kernel), against the oracle."""
+    rng = np.random.default_rng(40 + batch)
+    for k, n in ((3584, 768), (512, 65536)):
+        h = (rng.standard_normal((batch, k)) * 3).astype(F16)
+        g = (1 + 0.02 * rng.standard_normal(k)).astype(F16)
+        w = synth.gemv_weight(k, n, seed=41)
+        qo, so = oracle.quantize_w4(w)
+        xh = oracle.rmsnorm(h, g, 1e-6)
+        say("gemv norm prologue", batch, k, n)
+        y = torch.empty(batch, n, dtype=torch.float32, device="cuda")
+        nq.nq_gemv_w4a16(_packed_dev(w), n, k, 0, 0, batch, dev(h), dev(g), 1e-6, None, y, nq.NQ_EPI_STORE_F32)
+        assert rel_inf(host(y), oracle.gemv_w4a16(qo, so, xh)) < TOL_LAYER
+
+
 def test_gemv_rejects_bad_arguments():
     w = synth.gemv_weight(256, 32, seed=9)
     p = _packed_dev(w)

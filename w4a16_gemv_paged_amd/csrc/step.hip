@@ -294,7 +294,7 @@ __device__ __forceinline__ f4 ps_block(const u32x4& w, const half_t* xg, uint32_
 // Barriers each role passes at the end of a stage of the given kind (the
 // first barrier of a GEMV stage means "partial sums in LDS", the last one
 // "the next stage's input is staged"); before the first stage, one.
-__device__ __forceinline__ int ps_end_barriers(int kind) { return kind == K_LM ? 1 : 2; }
+__device__ __forceinline__ int ps_end_barriers(int kind) { return kind == K_LM ? 1 : kind == K_ATT ? 3 : 2; }
 
 // ---------------------------------------------------------------- streaming waves
 
@@ -646,6 +646,46 @@ __device__ __forceinline__ void ps_attention(const PsParams& p, const PsLds& s, 
 #pragma unroll
     for (int c = 0; c < VC; ++c) *reinterpret_cast<f4*>(&s.att_o[(aw * 16 + r16) * (D + 4) + 16 * c + 4 * g4]) = o[c];
     ps_barrier();  // attention partials in LDS
+    if (active) {
+      // this split: the four waves' partials merged per head, heads aw, aw + 4,
+      // ... on this wave (a lane takes columns lane + 64 c), then stored: the
+      // attention output itself with one split, else the split's (output,
+      // max, sum) of each head
+      constexpr int R = D + 4;      // a head's row of split partials: output, max, sum, pad
+      constexpr int NPH = D / 64;   // columns per head per lane
+      static_assert(D % 64 == 0, "whole columns per lane");
+      for (int h = aw; h < REP; h += kPsAtt) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int a = 0; a < kPsAtt; ++a) M = fmaxf(M, s.att_m[a * 16 + h]);
+        float Ls = 0.0f, Oh[NPH];
+#pragma unroll
+        for (int c = 0; c < NPH; ++c) Oh[c] = 0.0f;
+#pragma unroll
+        for (int a = 0; a < kPsAtt; ++a) {
+          const float ma = s.att_m[a * 16 + h];
+          const float f = ma == -INFINITY ? 0.0f : exp2f(ma - M);
+          Ls = fmaf(f, s.att_l[a * 16 + h], Ls);
+#pragma unroll
+          for (int c = 0; c < NPH; ++c) Oh[c] = fmaf(f, s.att_o[(a * 16 + h) * (D + 4) + lane + 64 * c], Oh[c]);
+        }
+        if (ap.S == 1) {
+#pragma unroll
+          for (int c = 0; c < NPH; ++c) {
+            const int d = lane + 64 * c;
+            st_h_sc1(hm(p.ao) + static_cast<int64_t>(j * REP + h) * D + d,
+                     ps_prescale(static_cast<half_t>(Ls > 0.0f ? Oh[c] / Ls : 0.0f), d));
+          }
+        } else {
+          float* part = p.apart + static_cast<int64_t>(j * kPsMaxSplits + sp) * REP * R + h * R;
+#pragma unroll
+          for (int c = 0; c < NPH; ++c) st_f_sc1(part + lane + 64 * c, Oh[c]);
+          if (lane < 2) st_f_sc1(part + D + lane, lane == 0 ? M : Ls);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the stores are complete before the control wave arrives
+    ps_barrier();  // split partials stored
     ps_barrier();  // O input staged
     for (int st = 0; st < 3; ++st)   // O, GU, D
       for (int b = 0; b < 2; ++b) ps_barrier();
@@ -796,56 +836,7 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
     // ---- attention: merge the attention waves' partials, then the splits
     ps_barrier();  // attention partials in LDS
     stamp(l, 3);
-    if (wg < p.nkv * ap.S) {
-      // this split: the attention waves' partials merged per head (a lane
-      // takes columns lane + 64 c of every head; the maxima, sums and weights
-      // are the same in every lane)
-      const int j = wg / ap.S, sp = wg % ap.S;
-      constexpr int R = D + 4;      // a head's row of split partials: output, max, sum, pad
-      constexpr int NPH = D / 64;   // columns per head per lane
-      static_assert(D % 64 == 0, "whole columns per lane");
-      float Mh[REP], Lh[REP], Oh[REP][NPH];
-#pragma unroll
-      for (int h = 0; h < REP; ++h) {
-        float M = -INFINITY;
-#pragma unroll
-        for (int a = 0; a < kPsAtt; ++a) M = fmaxf(M, s.att_m[a * 16 + h]);
-        float Ls = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NPH; ++c) Oh[h][c] = 0.0f;
-#pragma unroll
-        for (int a = 0; a < kPsAtt; ++a) {
-          const float ma = s.att_m[a * 16 + h];
-          const float f = ma == -INFINITY ? 0.0f : exp2f(ma - M);
-          Ls = fmaf(f, s.att_l[a * 16 + h], Ls);
-#pragma unroll
-          for (int c = 0; c < NPH; ++c) Oh[h][c] = fmaf(f, s.att_o[(a * 16 + h) * (D + 4) + lane + 64 * c], Oh[h][c]);
-        }
-        Mh[h] = M;
-        Lh[h] = Ls;
-      }
-      auto store_ao = [&]() {
-#pragma unroll
-        for (int h = 0; h < REP; ++h)
-#pragma unroll
-          for (int c = 0; c < NPH; ++c) {
-            const int d = lane + 64 * c;
-            st_h_sc1(hm(p.ao) + static_cast<int64_t>(j * REP + h) * D + d,
-                     ps_prescale(static_cast<half_t>(Lh[h] > 0.0f ? Oh[h][c] / Lh[h] : 0.0f), d));
-          }
-      };
-      if (ap.S == 1) {
-        store_ao();
-      } else {  // this split's (output, max, sum) of each head
-        float* part = p.apart + static_cast<int64_t>(j * kPsMaxSplits + sp) * REP * R;
-#pragma unroll
-        for (int h = 0; h < REP; ++h) {
-#pragma unroll
-          for (int c = 0; c < NPH; ++c) st_f_sc1(part + h * R + lane + 64 * c, Oh[h][c]);
-          if (lane < 2) st_f_sc1(part + h * R + D + lane, lane == 0 ? Mh[h] : Lh[h]);
-        }
-      }
-    }
+    ps_barrier();  // split partials stored (by the attention waves)
     if (ap.S > 1) {
       // Every split is in memory: each workgroup merges its share of the
       // outputs (m per workgroup) over the S splits. Lane i + m g (i < m

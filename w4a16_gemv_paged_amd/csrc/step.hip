@@ -156,6 +156,7 @@ struct PsLds {
   int* geo;        // [kPsStream][6 kinds][4] each streaming wave's stage geometry
   uint8_t* sca;    // the group scales of this workgroup's tiles: QKV, gate/up, LM head stages
   uint8_t* scb;    // O and down stages
+  float* rsv;      // the gate/up input's 1/rms, for the waves that share its epilogue
 };
 
 __device__ __forceinline__ PsLds ps_lds(unsigned char* smem, const PsParams& p) {
@@ -169,6 +170,7 @@ __device__ __forceinline__ PsLds ps_lds(unsigned char* smem, const PsParams& p) 
   s.geo = reinterpret_cast<int*>(s.att_o + kPsAtt * 16 * (p.hd + 4));
   s.sca = reinterpret_cast<uint8_t*>(s.geo + kPsStream * 6 * 4);
   s.scb = s.sca + p.sc_a;
+  s.rsv = reinterpret_cast<float*>(s.scb + p.sc_b);
   return s;
 }
 
@@ -291,10 +293,38 @@ __device__ __forceinline__ f4 ps_block(const u32x4& w, const half_t* xg, uint32_
   return d;
 }
 
+// A tile row's sum over its segments (row-major partials, segments padded to 4),
+// added in segment order.
+__device__ __forceinline__ float ps_tile_sum(const PsLds& s, const Geo& g0, int tl, int rr) {
+  const int sp = (g0.nseg + 3) & ~3;
+  const float* r = s.part + (tl * 16 + rr) * sp;
+  float v = 0.0f;
+  for (int q = 0; q < sp; q += 4) {
+    const f4 c = *reinterpret_cast<const f4*>(r + q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (q + e < g0.nseg) v += c[e];
+  }
+  return v;
+}
+
+// The gate/up epilogue's share of wave wi (0 the control wave, 1.. the
+// attention waves): a tile's 8 outputs, SwiGLU of its gate and up rows,
+// pre-scaled for the down projection.
+__device__ __forceinline__ void ps_gu_epilogue(const PsParams& p, const PsLds& s, int wi, float rs) {
+  const int lane = threadIdx.x & 63;
+  const Geo gg = ps_geo(p, K_GU, blockIdx.x, 0);
+  for (int i = wi * 64 + lane; i < gg.nt * 8; i += (1 + kPsAtt) * 64) {
+    const int tl = i / 8, rr = i & 7;
+    const float gv = ps_tile_sum(s, gg, tl, rr) * rs, uv = ps_tile_sum(s, gg, tl, rr + 8) * rs;
+    st_h_sc1(hm(p.act) + 8 * (gg.t0 + tl) + rr, ps_prescale(static_cast<half_t>(gv / (1.0f + expf(-gv)) * uv), rr));
+  }
+}
+
 // Barriers each role passes at the end of a stage of the given kind (the
 // first barrier of a GEMV stage means "partial sums in LDS", the last one
 // "the next stage's input is staged"); before the first stage, one.
-__device__ __forceinline__ int ps_end_barriers(int kind) { return kind == K_LM ? 1 : kind == K_ATT ? 3 : 2; }
+__device__ __forceinline__ int ps_end_barriers(int kind) { return kind == K_LM ? 1 : (kind == K_ATT || kind == K_GU) ? 3 : 2; }
 
 // ---------------------------------------------------------------- streaming waves
 
@@ -687,8 +717,15 @@ __device__ __forceinline__ void ps_attention(const PsParams& p, const PsLds& s, 
     __builtin_amdgcn_s_waitcnt(0);  // the stores are complete before the control wave arrives
     ps_barrier();  // split partials stored
     ps_barrier();  // O input staged
-    for (int st = 0; st < 3; ++st)   // O, GU, D
-      for (int b = 0; b < 2; ++b) ps_barrier();
+    ps_barrier();  // O partials
+    ps_barrier();  // gate/up input staged
+    ps_barrier();  // gate/up partials
+    ps_gu_epilogue(p, s, 1 + aw, *s.rsv);
+    __builtin_amdgcn_s_waitcnt(0);  // the stores are complete before the control wave arrives
+    ps_barrier();  // gate/up outputs stored
+    ps_barrier();  // down input staged
+    ps_barrier();  // down partials
+    ps_barrier();  // next stage's input staged
   }
   ps_barrier();  // LM partials
 }
@@ -752,19 +789,7 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
   ps_barrier();  // stage 0 input staged
   float rs = ps_rms(ss, p.H, p.eps);
 
-  // a tile row: its segments' sums, added in segment order
-  auto tile_sum = [&](const Geo& g0, int tl, int rr) {
-    const int sp = (g0.nseg + 3) & ~3;
-    const float* r = s.part + (tl * 16 + rr) * sp;
-    float v = 0.0f;
-    for (int q = 0; q < sp; q += 4) {
-      const f4 c = *reinterpret_cast<const f4*>(r + q);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (q + e < g0.nseg) v += c[e];
-    }
-    return v;
-  };
+  auto tile_sum = [&](const Geo& g0, int tl, int rr) { return ps_tile_sum(s, g0, tl, rr); };
 
   for (int l = 0; l < L; ++l) {
     const PsLayer& Ly = p.layer[l];
@@ -921,21 +946,15 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     ps_barrier();  // gate/up input staged
     rs = ps_rms(ss, p.H, p.eps);
+    if (lane == 0) *s.rsv = rs;  // for the attention waves' share of the epilogue (read after the next barrier)
 
     // ---- gate/up + SwiGLU
     ps_barrier();  // gate/up partials
     stamp(l, 9);
     if (l + 1 < L) ps_dma_scales(p, s.sca, K_QKV, l + 1);
     else ps_dma_scales(p, s.sca, K_LM, l);
-    {
-      // a tile's 8 outputs: SwiGLU of its gate and up rows, pre-scaled
-      const Geo gg = ps_geo(p, K_GU, wg, 0);
-      for (int i = lane; i < gg.nt * 8; i += 64) {
-        const int tl = i / 8, rr = i & 7;
-        const float gv = tile_sum(gg, tl, rr) * rs, uv = tile_sum(gg, tl, rr + 8) * rs;
-        st_h_sc1(hm(p.act) + 8 * (gg.t0 + tl) + rr, ps_prescale(static_cast<half_t>(gv / (1.0f + expf(-gv)) * uv), rr));
-      }
-    }
+    ps_gu_epilogue(p, s, 0, rs);
+    ps_barrier();  // gate/up outputs stored (the attention waves' share too)
     stamp(l, 10);
     ps_sync(p, ++epoch, x, li);
     stamp(l, 11);
@@ -1084,7 +1103,7 @@ size_t ps_lds_bytes(const PsParams& p) {
   const size_t xs = static_cast<size_t>(p.kmax + p.H) * 2;
   const size_t part = static_cast<size_t>(p.maxu) * 16 * 4;
   const size_t att = static_cast<size_t>(kPsAtt) * 16 * 4 * 2 + static_cast<size_t>(kPsAtt) * 16 * (p.hd + 4) * 4;
-  const size_t need = xs + part + att + kPsStream * 6 * 4 * 4 + static_cast<size_t>(p.sc_a) + p.sc_b;
+  const size_t need = xs + part + att + kPsStream * 6 * 4 * 4 + static_cast<size_t>(p.sc_a) + p.sc_b + 16;
   // at least 81 KiB: one workgroup per CU, whatever the registers allow
   return need < 96 * 1024 ? 96 * 1024 : need;
 }

@@ -217,6 +217,28 @@ __device__ void ps_sync(const PsParams& p, int target, int x, int li) {
   }
 }
 
+// Control wave: a barrier of the 32 workgroups of XCD x only. Their arrivals
+// (epoch ``target``) sit in the second cache line of the XCD's flag row, held
+// by the XCD's L2 like the first; bounded like ps_sync.
+__device__ void ps_xcd_sync(const PsParams& p, int target, int x, int li) {
+  const int lane = threadIdx.x & 63;
+  __builtin_amdgcn_s_waitcnt(0);
+  if (ld_sc1(p.abort) != 0) return;
+  int* row = p.xflag + x * 64 + kPsPerXcd;
+  if (lane == 0) st_xcd(row + li, target);
+  for (int it = 0; it < p.max_polls; ++it) {
+    bool mine = true;
+    if (lane < kPsPerXcd) mine = (ld_sc1(row + lane) - target) >= 0;
+    if (__all(mine)) return;
+    if ((it & 31) == 31 && ld_sc1(p.abort) != 0) return;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (lane == 0) {
+    st_sc1(p.abort, 1);
+    raise_flag(p.err, kAbortBit);
+  }
+}
+
 // Control wave: stage K fp16 values into LDS (DMA, 1 KiB per instruction);
 // sc1 for values written by other workgroups in this launch.
 __device__ __forceinline__ void ps_dma(half_t* dst, const half_t* src, int K, bool coherent) {
@@ -505,13 +527,16 @@ __device__ __forceinline__ void ps_streaming(const PsParams& p, const PsLds& s, 
 
 struct AttPlan {
   int len, npages, per, S;  // context length, pages, pages per split, splits per KV head
+  bool local;               // every split of a KV head on one XCD (slots 0..S-1 of XCD j * 8 / nkv)
 };
 
 // Splits of kPsSplitPages pages (one per attention wave) while there are
 // workgroups for them: a split's pages are dealt to the workgroup's attention
 // waves in turn, and a wave's pages are a chain of load latencies (two pages
-// in flight), while more splits cost only the merge spread over all
-// workgroups (one hand-off and a few loads per lane). At most kPsMaxSplits
+// in flight), while more splits cost only a few loads per lane of the merge.
+// Up to 32 splits per KV head sit on one XCD, whose workgroups merge them
+// after a barrier of that XCD alone; beyond that the splits spread over all
+// workgroups, which all merge after a full hand-off. At most kPsMaxSplits
 // splits per KV head and one workgroup per split; longer contexts take more
 // pages per split, up to 64 per wave.
 constexpr int kPsSplitPages = 4;
@@ -526,7 +551,27 @@ __device__ __forceinline__ AttPlan ps_att_plan(int len, int nkv) {
   per = (per + kPsAtt - 1) / kPsAtt * kPsAtt;
   a.per = per < kPsAtt ? kPsAtt : per;
   a.S = (a.npages + a.per - 1) / a.per;
+  a.local = a.S <= kPsPerXcd && kPsXcds % nkv == 0;
   return a;
+}
+
+// The (KV head j, split sp) of the workgroup in slot li of XCD x, if it has
+// one. With a local plan, KV head j's splits are slots 0..S-1 of XCD
+// j * 8 / nkv, so that their merge waits for that XCD alone; otherwise the
+// splits are dealt over the slots x * 32 + li in order.
+__device__ __forceinline__ bool ps_att_split(const AttPlan& ap, int nkv, int x, int li, int& j, int& sp) {
+  if (ap.local) {
+    const int step = kPsXcds / nkv;
+    if (x % step != 0 || li >= ap.S) return false;
+    j = x / step;
+    sp = li;
+    return true;
+  }
+  const int v = x * kPsPerXcd + li;
+  if (v >= nkv * ap.S) return false;
+  j = v / ap.S;
+  sp = v % ap.S;
+  return true;
 }
 
 constexpr int kPsAttRing = 2;  // pages in flight per attention wave
@@ -537,11 +582,16 @@ __device__ __forceinline__ void ps_attention(const PsParams& p, const PsLds& s, 
   constexpr int KJ = D / 32, VC = D / 16;
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int wg = blockIdx.x;
   const int L = p.L;
   const AttPlan ap = ps_att_plan(pos + 1, p.nkv);
-  const bool active = wg < p.nkv * ap.S && pos >= 0 && ap.npages <= p.max_pages;
-  const int j = active ? wg / ap.S : 0, sp = active ? wg % ap.S : 0;
+  // the XCD (hardware register XCC_ID) and, once the control wave has its
+  // ticket, the slot of this workgroup decide its split
+  const int x = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_s_getreg((31 << 11) | 20) & 0xf) & (kPsXcds - 1);
+  ps_barrier();  // the first stage's input is staged (and the slot is in LDS)
+  const int li = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(s.rsv)[1]);
+  int j = 0, sp = 0;
+  const bool active = ps_att_split(ap, p.nkv, x, li, j, sp) && pos >= 0 && ap.npages <= p.max_pages;
+  if (!active) j = sp = 0;
   const int p0 = sp * ap.per, p1 = min(ap.npages, p0 + ap.per);
   // this wave's pages: p0 + aw + k * kPsAtt for k < nmine (at most 64)
   const int nmine = active && p0 + aw < p1 ? (p1 - p0 - aw + kPsAtt - 1) / kPsAtt : 0;
@@ -553,7 +603,6 @@ __device__ __forceinline__ void ps_attention(const PsParams& p, const PsLds& s, 
   if (lane < nmine) pid_reg = p.pt[p0 + aw + lane * kPsAtt];
   auto page_id = [&](int k) { return __builtin_amdgcn_readlane(pid_reg, k & 63); };
 
-  ps_barrier();  // the first stage's input is staged
   for (int l = 0; l < L; ++l) {
     const size_t lbase = static_cast<size_t>(l) * 2 * p.layer_pool;
     const half_t* kp = hc(p.kpool) + lbase;
@@ -748,6 +797,61 @@ __device__ __forceinline__ void ps_dma_scales(const PsParams& p, uint8_t* dst, i
   }
 }
 
+// Control wave: the attention outputs [o0, o0 + m) (below oend) merged over
+// the S splits in memory and stored pre-scaled. Lane i + m g (i < m outputs,
+// g < G groups) takes splits g, g + G, ... of output i, four at a time (their
+// loads issued together); the G groups are then merged in group order.
+template <int D, int REP>
+__device__ __forceinline__ void ps_merge_splits(const PsParams& p, int S, int o0, int oend, int m, int G) {
+  const int lane = threadIdx.x & 63;
+  constexpr int R = D + 4;
+  const int i = lane % m, g = lane / m;
+  const int o = o0 + i;
+  float M = -INFINITY, Ls = 0.0f, O = 0.0f;
+  if (g < G && o < oend) {
+    const int head = o / D, d = o % D, j = head / REP, h = head % REP;
+    const float* pb = p.apart + static_cast<int64_t>(j * kPsMaxSplits) * REP * R + h * R;
+    for (int q0 = g; q0 < S; q0 += 4 * G) {
+      float mq[4], lq[4], oq[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + G * u;
+        mq[u] = -INFINITY;
+        lq[u] = oq[u] = 0.0f;
+        if (q < S) {
+          const float* r = pb + static_cast<int64_t>(q) * REP * R;
+          mq[u] = ld_f_sc1(r + D);
+          lq[u] = ld_f_sc1(r + D + 1);
+          oq[u] = ld_f_sc1(r + d);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (mq[u] != -INFINITY) {
+          const float Mn = fmaxf(M, mq[u]);
+          const float a = M == -INFINITY ? 0.0f : exp2f(M - Mn), b = exp2f(mq[u] - Mn);
+          Ls = Ls * a + lq[u] * b;
+          O = O * a + oq[u] * b;
+          M = Mn;
+        }
+      }
+    }
+  }
+  // the G groups of output i, in group order (lanes i, i + m, ...)
+  float Mt = __shfl(M, i), Lt = __shfl(Ls, i), Ot = __shfl(O, i);
+  for (int gg = 1; gg < G; ++gg) {
+    const float mg = __shfl(M, i + gg * m), lg = __shfl(Ls, i + gg * m), og = __shfl(O, i + gg * m);
+    if (mg != -INFINITY) {
+      const float Mn = fmaxf(Mt, mg);
+      const float a = Mt == -INFINITY ? 0.0f : exp2f(Mt - Mn), b = exp2f(mg - Mn);
+      Lt = Lt * a + lg * b;
+      Ot = Ot * a + og * b;
+      Mt = Mn;
+    }
+  }
+  if (g == 0 && o < oend) st_h_sc1(hm(p.ao) + o, ps_prescale(static_cast<half_t>(Lt > 0.0f ? Ot / Lt : 0.0f), o % D));
+}
+
 template <int D, int REP>
 __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, int pos, int tok, int x,
                                            int slot_ticket) {
@@ -759,6 +863,7 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
   // hand-offs every workgroup has passed
   const int li = slot_ticket % kPsPerXcd;
   int epoch = __builtin_amdgcn_readfirstlane(ld_sc1(p.xflag + x * 64 + li));
+  int xepoch = __builtin_amdgcn_readfirstlane(ld_sc1(p.xflag + x * 64 + kPsPerXcd + li));  // XCD-local barriers
   const AttPlan ap = ps_att_plan(pos + 1, p.nkv);
   const int qkv_n = (p.nh + 2 * p.nkv) * D;
   // optional stage stamps (realtime counter, 100 MHz): row l of this
@@ -785,6 +890,7 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
   __builtin_amdgcn_s_waitcnt(0);
   if (go.nt > 0 && lane < 16) hres = s.xs[go.t0 * 16 + lane];
   float ss = ps_stage_gain(s.xs, s.gs, p.H);
+  if (lane == 0) reinterpret_cast<int*>(s.rsv)[1] = li;  // for the attention waves
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   ps_barrier();  // stage 0 input staged
   float rs = ps_rms(ss, p.H, p.eps);
@@ -863,62 +969,20 @@ __device__ __forceinline__ void ps_control(const PsParams& p, const PsLds& s, in
     stamp(l, 3);
     ps_barrier();  // split partials stored (by the attention waves)
     if (ap.S > 1) {
-      // Every split is in memory: each workgroup merges its share of the
-      // outputs (m per workgroup) over the S splits. Lane i + m g (i < m
-      // outputs, g < 4 groups) takes splits g, g + 4, ... of output i, four at
-      // a time (their loads issued together); the four groups are then merged
-      // in group order.
-      ps_sync(p, ++epoch, x, li);
-      constexpr int R = D + 4;
-      const int nout = p.nh * D;
-      const int m = (nout + kPsWG - 1) / kPsWG;  // outputs per workgroup (4 m <= 64: nh * D <= 4096)
-      const int i = lane % m, g = lane / m;
-      const int o = wg * m + i;
-      float M = -INFINITY, Ls = 0.0f, O = 0.0f;
-      if (g < 4 && o < nout) {
-        const int head = o / D, d = o % D, j = head / REP, h = head % REP;
-        const float* pb = p.apart + static_cast<int64_t>(j * kPsMaxSplits) * REP * R + h * R;
-        for (int q0 = g; q0 < ap.S; q0 += 16) {
-          float mq[4], lq[4], oq[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int q = q0 + 4 * u;
-            mq[u] = -INFINITY;
-            lq[u] = oq[u] = 0.0f;
-            if (q < ap.S) {
-              const float* r = pb + static_cast<int64_t>(q) * REP * R;
-              mq[u] = ld_f_sc1(r + D);
-              lq[u] = ld_f_sc1(r + D + 1);
-              oq[u] = ld_f_sc1(r + d);
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (mq[u] != -INFINITY) {
-              const float Mn = fmaxf(M, mq[u]);
-              const float a = M == -INFINITY ? 0.0f : exp2f(M - Mn), b = exp2f(mq[u] - Mn);
-              Ls = Ls * a + lq[u] * b;
-              O = O * a + oq[u] * b;
-              M = Mn;
-            }
-          }
-        }
+      // Every split is in memory. With a local plan, the 32 workgroups of each
+      // KV head's XCD merge that head's outputs (the others go on to the
+      // hand-off); otherwise every workgroup merges its share of all outputs.
+      if (!ap.local) {
+        ps_sync(p, ++epoch, x, li);
+        const int m = (p.nh * D + kPsWG - 1) / kPsWG;  // 4 m <= 64: nh * D <= 4096
+        ps_merge_splits<D, REP>(p, ap.S, wg * m, p.nh * D, m, 4);
+      } else if (x % (kPsXcds / p.nkv) == 0) {
+        ps_xcd_sync(p, ++xepoch, x, li);
+        constexpr int m = (REP * D + kPsPerXcd - 1) / kPsPerXcd;
+        static_assert(m <= 64, "a lane per output");
+        const int o0 = x / (kPsXcds / p.nkv) * REP * D;
+        ps_merge_splits<D, REP>(p, ap.S, o0 + li * m, o0 + REP * D, m, 64 / m < 4 ? 64 / m : 4);
       }
-      // the four groups of output i, in group order (lanes i, i + m, ...)
-      float Mt = __shfl(M, i), Lt = __shfl(Ls, i), Ot = __shfl(O, i);
-#pragma unroll
-      for (int gg = 1; gg < 4; ++gg) {
-        const float mg = __shfl(M, i + gg * m), lg = __shfl(Ls, i + gg * m), og = __shfl(O, i + gg * m);
-        if (mg != -INFINITY) {
-          const float Mn = fmaxf(Mt, mg);
-          const float a = Mt == -INFINITY ? 0.0f : exp2f(Mt - Mn), b = exp2f(mg - Mn);
-          Lt = Lt * a + lg * b;
-          Ot = Ot * a + og * b;
-          Mt = Mn;
-        }
-      }
-      if (g == 0 && o < nout)
-        st_h_sc1(hm(p.ao) + o, ps_prescale(static_cast<half_t>(Lt > 0.0f ? Ot / Lt : 0.0f), o % D));
     }
     stamp(l, 4);
     ps_sync(p, ++epoch, x, li);

@@ -757,9 +757,15 @@ __device__ __forceinline__ void ps_attention(const PsParams& p, const PsLds& s, 
           }
         } else {
           float* part = p.apart + static_cast<int64_t>(j * kPsMaxSplits + sp) * REP * R + h * R;
+          if (ap.local) {  // read on this XCD only: plain stores, held by its L2
 #pragma unroll
-          for (int c = 0; c < NPH; ++c) st_f_sc1(part + lane + 64 * c, Oh[c]);
-          if (lane < 2) st_f_sc1(part + D + lane, lane == 0 ? M : Ls);
+            for (int c = 0; c < NPH; ++c) part[lane + 64 * c] = Oh[c];
+            if (lane < 2) part[D + lane] = lane == 0 ? M : Ls;
+          } else {
+#pragma unroll
+            for (int c = 0; c < NPH; ++c) st_f_sc1(part + lane + 64 * c, Oh[c]);
+            if (lane < 2) st_f_sc1(part + D + lane, lane == 0 ? M : Ls);
+          }
         }
       }
     }

@@ -603,37 +603,39 @@ __device__ __forceinline__ void ps_attention(const PsParams& p, const PsLds& s, 
   if (lane < nmine) pid_reg = p.pt[p0 + aw + lane * kPsAtt];
   auto page_id = [&](int k) { return __builtin_amdgcn_readlane(pid_reg, k & 63); };
 
-  for (int l = 0; l < L; ++l) {
-    const size_t lbase = static_cast<size_t>(l) * 2 * p.layer_pool;
-    const half_t* kp = hc(p.kpool) + lbase;
+  // Page k of layer l's K and V into registers, with sc1 loads (coherent with
+  // the other XCDs' stores of this step's token; the pages are read once per
+  // step, so bypassing the XCD's L2 costs nothing). Past the wave's last page
+  // the loads take a zero-length descriptor: they return zeros and touch no
+  // memory, so every page slot issues the same loads and the waits stay exact.
+  auto load_l = [&](int l, int k, half8 (&kf)[KJ], half4 (&vf)[VC]) {
+    const half_t* kp = hc(p.kpool) + static_cast<size_t>(l) * 2 * p.layer_pool;
     const half_t* vp = kp + p.layer_pool;
-    // Page k's K and V into registers, with sc1 loads (coherent with the
-    // other XCDs' stores of this step's token; the pages are read once per
-    // step, so bypassing the XCD's L2 costs nothing). Past the wave's last page
-    // the loads take a zero-length descriptor: they return zeros and touch no
-    // memory, so every page slot issues the same loads and the waits stay exact.
-    auto load = [&](int k, half8 (&kf)[KJ], half4 (&vf)[VC]) {
-      const int id = page_id(k);
-      const bool ok = k < nmine && id >= 0 && id < p.num_pages;
-      const int64_t base = (static_cast<int64_t>(ok ? id : 0) * p.nkv + j) * (kPageTokens * D);
-      const uint32_t bytes = ok ? kPageTokens * D * 2 : 0;
-      const __amdgpu_buffer_rsrc_t kr = rsrc(kp + base, bytes);
-      const __amdgpu_buffer_rsrc_t vr = rsrc(vp + base, bytes);
+    const int id = page_id(k);
+    const bool ok = k < nmine && id >= 0 && id < p.num_pages;
+    const int64_t base = (static_cast<int64_t>(ok ? id : 0) * p.nkv + j) * (kPageTokens * D);
+    const uint32_t bytes = ok ? kPageTokens * D * 2 : 0;
+    const __amdgpu_buffer_rsrc_t kr = rsrc(kp + base, bytes);
+    const __amdgpu_buffer_rsrc_t vr = rsrc(vp + base, bytes);
 #pragma unroll
-      for (int jj = 0; jj < KJ; ++jj)
-        kf[jj] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(kr, (r16 * D + 8 * g4 + 32 * jj) * 2, 0, kSc1));
+    for (int jj = 0; jj < KJ; ++jj)
+      kf[jj] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(kr, (r16 * D + 8 * g4 + 32 * jj) * 2, 0, kSc1));
 #pragma unroll
-      for (int c = 0; c < VC; ++c)
-        vf[c] = __builtin_bit_cast(half4, __builtin_amdgcn_raw_buffer_load_b64(vr, ((16 * c + r16) * kPageTokens + 4 * g4) * 2, 0, kSc1));
-    };
-    half8 kA[kPsAttRing][KJ];
-    half4 vA[kPsAttRing][VC];
-    // the first pages are requested before the QKV results exist, unless the
-    // wave holds this step's token
-    if (!fresh) {
+    for (int c = 0; c < VC; ++c)
+      vf[c] = __builtin_bit_cast(half4, __builtin_amdgcn_raw_buffer_load_b64(vr, ((16 * c + r16) * kPageTokens + 4 * g4) * 2, 0, kSc1));
+  };
+  // A layer's first pages are requested long before its QKV results exist
+  // (layer 0's here, the next layer's once this one's gate/up outputs are
+  // stored), unless the wave holds this step's token.
+  half8 kA[kPsAttRing][KJ];
+  half4 vA[kPsAttRing][VC];
+  if (!fresh) {
 #pragma unroll
-      for (int r = 0; r < kPsAttRing; ++r) load(r, kA[r], vA[r]);
-    }
+    for (int r = 0; r < kPsAttRing; ++r) load_l(0, r, kA[r], vA[r]);
+  }
+
+  for (int l = 0; l < L; ++l) {
+    auto load = [&](int k, half8 (&kf)[KJ], half4 (&vf)[VC]) { load_l(l, k, kf, vf); };
 
     ps_barrier();  // QKV partials
     ps_barrier();  // q and this step's K/V are everywhere
@@ -777,6 +779,10 @@ __device__ __forceinline__ void ps_attention(const PsParams& p, const PsLds& s, 
     ps_barrier();  // gate/up partials
     ps_gu_epilogue(p, s, 1 + aw, *s.rsv);
     __builtin_amdgcn_s_waitcnt(0);  // the stores are complete before the control wave arrives
+    if (l + 1 < L && !fresh) {
+#pragma unroll
+      for (int r = 0; r < kPsAttRing; ++r) load_l(l + 1, r, kA[r], vA[r]);
+    }
     ps_barrier();  // gate/up outputs stored
     ps_barrier();  // down input staged
     ps_barrier();  // down partials

@@ -271,19 +271,33 @@ __device__ __forceinline__ half_t ps_prescale(half_t v, int k) {
 __device__ __forceinline__ float ps_stage_gain(half_t* xs, const half_t* gs, int K) {
   const int lane = threadIdx.x & 63;
   const h2 sixteenth = {static_cast<half_t>(0.0625f), static_cast<half_t>(0.0625f)};
+  constexpr int kBatch = 4;  // items read before any is written back: one LDS latency per batch
   float ss = 0.0f;
-  for (int i = lane; i < K / 8; i += 64) {
-    uint4 v = *reinterpret_cast<const uint4*>(xs + i * 8);
-    const uint4 gv = *reinterpret_cast<const uint4*>(gs + i * 8);
-    h2* x = reinterpret_cast<h2*>(&v);
-    const h2* g = reinterpret_cast<const h2*>(&gv);
+  for (int i0 = lane; i0 < K / 8; i0 += 64 * kBatch) {
+    uint4 v[kBatch], gv[kBatch];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ss = __builtin_amdgcn_fdot2(x[q], x[q], ss, false);
-    x[0] = x[0] * g[0];
-    x[1] = x[1] * (g[1] * sixteenth);
-    x[2] = x[2] * g[2];
-    x[3] = x[3] * (g[3] * sixteenth);
-    *reinterpret_cast<uint4*>(xs + i * 8) = v;
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = i0 + 64 * k;
+      if (i < K / 8) {
+        v[k] = *reinterpret_cast<const uint4*>(xs + i * 8);
+        gv[k] = *reinterpret_cast<const uint4*>(gs + i * 8);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = i0 + 64 * k;
+      if (i < K / 8) {
+        h2* x = reinterpret_cast<h2*>(&v[k]);
+        const h2* g = reinterpret_cast<const h2*>(&gv[k]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ss = __builtin_amdgcn_fdot2(x[q], x[q], ss, false);
+        x[0] = x[0] * g[0];
+        x[1] = x[1] * (g[1] * sixteenth);
+        x[2] = x[2] * g[2];
+        x[3] = x[3] * (g[3] * sixteenth);
+        *reinterpret_cast<uint4*>(xs + i * 8) = v[k];
+      }
+    }
   }
   return ss;
 }

@@ -195,9 +195,10 @@ def test_split_attention_long_context(tiny):
     """Batch 1 over 64-page tables, 200-token prompt (13-14 pages in use). One
     kernel per stage: the pages split over 16 workgroups per KV head (4 pages
     each, one per wave; four splits hold pages, the rest are empty) whose
-    partials the combine kernel merges. Persistent step: one split of all the
-    pages per KV head. Logits and tokens against the oracle; graph replay
-    equals eager bitwise."""
+    partials the combine kernel merges. Persistent step: four splits of 4 pages
+    per KV head, on XCD 0 for the first KV head and XCD 4 for the second, whose
+    32 workgroups merge the head's outputs after a barrier of that XCD alone.
+    Logits and tokens against the oracle; graph replay equals eager bitwise."""
     om, dm = tiny
     prompt = synth.prompt_ids(200, SHAPE.vocab, seed=60)
     say("tiny long-context eager run")
@@ -217,7 +218,8 @@ def test_split_attention_long_context(tiny):
 def test_split_attention_many_splits(tiny):
     """Batch 1 at a 2500-token context (157 pages): the persistent step splits
     each KV head's pages 40 ways (4 pages per workgroup, one per attention
-    wave), and every workgroup merges two outputs over the 40 splits (the tiny
+    wave), more than one XCD's 32 workgroups, so after a hand-off across all
+    XCDs every workgroup merges two outputs over the 40 splits (the tiny
     model's 512 outputs over 256 workgroups), ten per lane in three batches of
     loads. Logits and tokens against the oracle."""
     om, dm = tiny

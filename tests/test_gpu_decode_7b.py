@@ -14,7 +14,8 @@ over the full vocabulary at every generated step.
   attention splits the pages over 13 workgroups per KV head (9-10 of them
   live) and the combine kernel merges them; the persistent batch-1 step splits
   each KV head's 33-38 live pages 9-10 ways (4 pages per workgroup, one per
-  attention wave) and every workgroup merges its share of the outputs.
+  attention wave), all on one XCD per KV head, whose 32 workgroups merge that
+  head's outputs after a barrier of that XCD alone.
 
 Every test runs in both step modes ("auto": batch 1 as the persistent
 whole-step kernel; "kernels": one kernel per stage).

@@ -234,6 +234,26 @@ def test_split_attention_many_splits(tiny):
     np.testing.assert_array_equal(gpu["tokens"][0][ok], orc["tokens"][ok])
 
 
+def test_split_attention_local_to_global_merge(tiny):
+    """Batch 1 from a 2040-token prompt through 16 generated tokens (contexts
+    2041-2056): the persistent step splits each KV head's pages into at most
+    32 splits of 4 pages, all on one XCD and merged after a barrier of that XCD
+    alone, while the context is at most 2048 tokens (128 pages); from 2049
+    tokens on 33 splits no longer fit one XCD's 32 workgroups, and every
+    workgroup merges its share after a hand-off across all XCDs. Every step's
+    logits against the oracle, and the tokens where the margin is clear."""
+    om, dm = tiny
+    prompt = synth.prompt_ids(2040, SHAPE.vocab, seed=62)
+    say("tiny 2040-token context run")
+    gpu = _run(dm, [prompt], 16, layers=False)
+    orc = oracle.generate(om, prompt, 16, forced=gpu["tokens"][0])
+    gl = gpu["logits"][len(prompt) - 1:, 0]
+    errs = [rel_inf(gl[i], orc["logits"][i]) for i in range(16)]
+    assert max(errs) < TOL_LOGITS, max(errs)
+    ok = orc["margins"] > MARGIN
+    np.testing.assert_array_equal(gpu["tokens"][0][ok], orc["tokens"][ok])
+
+
 def test_split_attention_batch8(tiny):
     """Batch 8 over 64-page tables: ragged prompts of 90-300 tokens span one to
     three splits of the pages."""

@@ -501,10 +501,16 @@ __device__ __forceinline__ void ps_streaming(const PsParams& p, const PsLds& s, 
       scale_acc(acc, ps_block(w, xg + i * kGroup, magic, nbias), *reinterpret_cast<const u32x2*>(sg + 32 * i));
     };
     if (len == kPsSeg) {
-      blk(w0, 0);
-      blk(w1, 1);
-      blk(w2, 2);
-      blk(w3, 3);
+      // block i's scale is applied while block i + 1 is on the matrix cores
+      auto sc = [&](int i) { return *reinterpret_cast<const u32x2*>(sg + 32 * i); };
+      const f4 d0 = ps_block(w0, xg, magic, nbias);
+      const f4 d1 = ps_block(w1, xg + kGroup, magic, nbias);
+      scale_acc(acc, d0, sc(0));
+      const f4 d2 = ps_block(w2, xg + 2 * kGroup, magic, nbias);
+      scale_acc(acc, d1, sc(1));
+      const f4 d3 = ps_block(w3, xg + 3 * kGroup, magic, nbias);
+      scale_acc(acc, d2, sc(2));
+      scale_acc(acc, d3, sc(3));
     } else {  // a tile's short last segment (len >= 1)
       blk(w0, 0);
       if (len > 1) blk(w1, 1);

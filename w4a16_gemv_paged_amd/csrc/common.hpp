@@ -181,7 +181,7 @@ struct PsParams {
   int32_t* err;
   float eps;
   // workspace: hand-off flags, counters and buffers
-  int* xflag;                       // [8][64] per-workgroup epochs, one row per XCD
+  int* xflag;                       // [8][64] per-workgroup epochs, one row per XCD: 0-31 hand-offs, 32-63 XCD-only barriers
   int* xcdflag;                     // [8 reading XCDs][8 XCDs][16] per-XCD epochs, a line each
   int* cnt;                         // [16][16] row 14: per-XCD slot tickets; row 15: LM head
   int* abort;

@@ -12,23 +12,27 @@
 //
 // Roles inside a workgroup of kPsWaves waves:
 //   * streaming waves 0..kPsStream-1: W4A16 GEMV blocks (the INT4 unpack and
-//     matrix-core products of the multi-kernel GEMV; the RMSNorm gain and the
-//     1/16 pre-scale of the biased codes are applied to the activations as
-//     they are read from LDS), partial sums per tile into LDS;
+//     matrix-core products of the multi-kernel GEMV, on activations staged in
+//     LDS with the RMSNorm gain and the 1/16 pre-scale of the biased codes
+//     already applied), partial sums per tile into LDS;
 //   * the control wave: epilogues (bias, RoPE, KV-page write, residual,
 //     SwiGLU, logits and greedy choice), the hand-off of every stage's output
 //     to all workgroups, and the staging of the next stage's input in LDS;
 //   * attention waves: split-K paged decode attention of one split of the
-//     pages of one KV head (GQA heads as the matrix-core columns).
+//     pages of one KV head (GQA heads as the matrix-core columns), the merge
+//     of their split's heads and its stores, and a share of the SwiGLU
+//     epilogue.
 //
 // Hand-offs between workgroups: a stage's outputs are written with sc1 stores
 // (coherent across the XCDs' L2s), then a hierarchical barrier: each
 // workgroup stores its arrival in a flag its XCD's L2 holds, the first
 // workgroup of each XCD publishes the XCD's arrival once all of its 32
 // workgroups are in, and every workgroup waits for the 8 XCD flags; the inputs
-// are then read with sc1 loads. Every wait is bounded: a wait that runs out
-// sets error bit 16 and an abort flag, and all later waits return at once, so
-// every wave always reaches the end of the kernel.
+// are then read with sc1 loads. While a KV head's attention splits fit one
+// XCD they all run there, and their merge waits for that XCD's workgroups
+// only (plain stores and a flag in that XCD's L2). Every wait is bounded: a
+// wait that runs out sets error bit 16 and an abort flag, and all later waits
+// return at once, so every wave always reaches the end of the kernel.
 #include <mutex>
 
 #include "device.hpp"

@@ -985,7 +985,8 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
 // about the same number of pages, and the grid (hence a captured graph) does
 // not depend on the lengths. Workgroups are 4 waves, so that three of them
 // fit on a CU at the kernel's register count: 12 waves per CU where one
-// 8-wave workgroup gives 8, and a finer grain for ragged batches.
+// 8-wave workgroup gives 8. A batch of one fills the CUs three times over; a
+// larger batch takes one workgroup per CU, whose longer splits stream faster.
 
 constexpr int kAttnWaves = 4;
 constexpr int kMaxPagesPerWave = 128;  // a split holds at most kAttnWaves * 128 pages
@@ -994,7 +995,13 @@ constexpr int kPidRegs = (kMaxPagesPerWave + 63) / 64;  // page ids held one per
 // whole workgroups of kAttnWaves waves on the 4 SIMDs of a CU
 constexpr int kAttnWavesPerSimd = kAttnWaves == 4 ? 3 : 2;
 static_assert(kAttnMaxSplits % 64 == 0, "combine weight slots");
-constexpr int kAttnTargetGroups = 768;  // three 4-wave workgroups per CU
+constexpr int kAttnTargetGroups = 768;  // batch 1: three 4-wave workgroups per CU
+// Batches of several sequences: one 4-wave workgroup per CU, each with longer
+// splits. The batch-8 step at 1.4k-16k context took 2.635 ms/step with 256
+// workgroups, 2.652 with 512 and 2.689 with 768 (same box); 128, 192, 384 and
+// 640, which leave CUs idle or unevenly loaded, took 3.10, 2.87, 2.85 and 2.79,
+// and 256 workgroups of 8 waves 2.669.
+constexpr int kAttnBatchGroups = 256;
 
 // Pages per split for S workgroups per KV head over B sequences holding P
 // pages in all: the fewest such that sum_b ceil(pages_b / per) <= S (each ceil
@@ -1015,7 +1022,7 @@ AttnPlan attn_plan(int32_t batch, int32_t n_kv, int32_t max_pages) {
     return p;
   }
   const int pages4 = (max_pages + kAttnWaves - 1) / kAttnWaves;
-  const int target = std::max(1, kAttnTargetGroups / std::max(1, n_kv));
+  const int target = std::max(1, (batch == 1 ? kAttnTargetGroups : kAttnBatchGroups) / std::max(1, n_kv));
   if (max_pages <= kAttnWaves || (batch == 1 && pages4 <= target)) {
     // fixed splits of one page per wave (one split when the table is that
     // short): the page ids do not wait for the length, and a batch of one

@@ -204,7 +204,7 @@ def test_attention_split_plan_sizes():
     """The split plan behind nq_attn_workspace_bytes (partials are
     [B][n_heads][S][d] and [B][n_heads][S][2] floats, each 256-byte aligned):
     batch 1 takes fixed splits of 4 pages (one per wave) while they number at
-    most 768 / n_kv; larger batches split by length over min(768 / n_kv,
+    most 768 / n_kv; larger batches split by length over min(256 / n_kv,
     B * ceil(pages / 4)) workgroups per KV head, at least B + 1; beyond 1024
     workgroups of 512 pages, or 64 sequences, nothing."""
     import synth
@@ -222,7 +222,7 @@ def test_attention_split_plan_sizes():
     assert nq.nq_attn_workspace_bytes(cfg, 1, 2048) == ws(1, 192)
     assert nq.nq_attn_workspace_bytes(cfg, 2, 8) == ws(2, 4)        # 2 * ceil(8 / 4) splits
     assert nq.nq_attn_workspace_bytes(cfg, 8, 3) == ws(8, 1)        # tables of at most 4 pages: unsplit
-    assert nq.nq_attn_workspace_bytes(cfg, 8, 2048) == ws(8, 192)
+    assert nq.nq_attn_workspace_bytes(cfg, 8, 2048) == ws(8, 64)     # one workgroup per CU over the 4 KV heads
     assert nq.nq_attn_workspace_bytes(cfg, 8, 32768) == ws(8, 520)  # 8 * 32768 / 512 + 8: no split over 512 pages
     assert nq.nq_attn_workspace_bytes(cfg, 65, 64) == 0
     assert nq.nq_attn_workspace_bytes(cfg, 64, 32768) == 0
@@ -292,8 +292,8 @@ def test_static_attention_refuses_beyond_its_scratch_without_gpu():
     kv = nq.nq_kv_alloc(cfg, fake, nq.nq_kv_pool_bytes(cfg, num_pages), num_pages)
     try:
         assert nq.NQ_ATTN_SCRATCH_BYTES == 24 << 20
-        assert nq.nq_attn_workspace_bytes(cfg, 8, 2048) <= nq.NQ_ATTN_SCRATCH_BYTES      # batch 8, 192 splits fit
-        for batch, pages in ((16, 2048), (64, 512), (64, 32768)):
+        assert nq.nq_attn_workspace_bytes(cfg, 8, 2048) <= nq.NQ_ATTN_SCRATCH_BYTES      # batch 8, 64 splits fit
+        for batch, pages in ((32, 2048), (64, 512), (64, 32768)):
             need = nq.nq_attn_workspace_bytes(cfg, batch, pages)
             assert need == 0 or need > nq.NQ_ATTN_SCRATCH_BYTES
             with pytest.raises(nq.NQError) as e:

@@ -297,8 +297,31 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
     }
     // (4) the scale of block i is applied while block i+1 is on the matrix
     //     cores; the next scale window is requested a window ahead
-    for (int ib = 0; ib < n_c; ib += kDepth) {
+    //     Windows with a later one refill every slot they consume (a block
+    //     past the wave's last reads past the tile and returns 0), so every
+    //     path has the same loads in flight and the compiler's wait for a
+    //     block counts only what is older than it; the last window refills
+    //     nothing.
+    int ib = 0;
+    for (; ib + kDepth < n_c; ib += kDepth) {
       const u32x2 snext = load_scales(ib + kDepth);
+      f4 dprev;
+      u32x2 sprev;
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const int i = ib + u;
+        const f4 d = gemv_block_mfma<GAIN>(wv[u], xlane + (ksi + p.ks * i) * xstep, magic, nbias);
+        if (u > 0) scale_acc(acc, dprev, sprev);
+        dprev = d;
+        sprev = row_bcast2(swin, u);
+        const int gn = c0 + ksi + p.ks * (i + kDepth);
+        wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff, i + kDepth < n_c ? gn * kBlockBytes : wbytes,
+                                                      kStreamOnce);
+      }
+      scale_acc(acc, dprev, sprev);
+      swin = snext;
+    }
+    if (ib < n_c) {
       f4 dprev;
       u32x2 sprev;
 #pragma unroll
@@ -309,14 +332,9 @@ __global__ __launch_bounds__(1024) void gemv_w4a16_kernel(GemvParams p) {
           if (u > 0) scale_acc(acc, dprev, sprev);
           dprev = d;
           sprev = row_bcast2(swin, u);
-          if (i + kDepth < n_c) {  // refill the slot just consumed
-            const int gn = c0 + ksi + p.ks * (i + kDepth);
-            wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wvoff, gn * kBlockBytes, kStreamOnce);
-          }
         }
       }
       scale_acc(acc, dprev, sprev);
-      swin = snext;
     }
   };
   if (p.ch >= p.G) {

@@ -200,37 +200,47 @@ __global__ __launch_bounds__(1024) void gemv_w4a8_kernel(A8Params p) {
   const int xstep = col < B ? kGroup : 0;
   const int mcol = col < B ? col : 0;
   f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int ib = 0; ib < n_c; ib += kA8Depth) {
+  auto block = [&](const int u, const int i) {
+    const int g = ksi + p.ks * i;
+    const uint8_t* xg = xlane + g * xstep;
+    const u32x4 w = wv[u];
+    i32x4 d = {0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const uint32_t w0 = w[2 * m], w1 = w[2 * m + 1];
+      const i32x4 a = {static_cast<int>(w0 & 0x0F0F0F0Fu), static_cast<int>((w0 >> 4) & 0x0F0F0F0Fu),
+                       static_cast<int>(w1 & 0x0F0F0F0Fu), static_cast<int>((w1 >> 4) & 0x0F0F0F0Fu)};
+      const i32x4 bx = *reinterpret_cast<const i32x4*>(xg + 16 * m);
+      d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx, d, 0, 0, 0);
+    }
+    const A8Meta mt = meta[mcol * G + g];
+    const float sx = col < B ? mt.s : 0.0f;
+    const int off = 8 * mt.sum;
+    const f4 f = {static_cast<float>(d[0] - off) * sx, static_cast<float>(d[1] - off) * sx,
+                  static_cast<float>(d[2] - off) * sx, static_cast<float>(d[3] - off) * sx};
+    scale_acc(acc, f, row_bcast2(swin, u));
+  };
+  // Every window but the last refills each slot it consumes, on every path (a
+  // block past the wave's last reads past the tile and returns 0): the loads
+  // in flight are then the same on every path, and the compiler's wait for a
+  // block counts only what is older than it. The last window refills nothing.
+  int ib = 0;
+  for (; ib + kA8Depth < n_c; ib += kA8Depth) {
     const u32x2 snext = load_scales(ib + kA8Depth);
 #pragma unroll
     for (int u = 0; u < kA8Depth; ++u) {
       const int i = ib + u;
-      if (i < n_c) {
-        const int g = ksi + p.ks * i;
-        const uint8_t* xg = xlane + g * xstep;
-        const u32x4 w = wv[u];
-        i32x4 d = {0, 0, 0, 0};
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const uint32_t w0 = w[2 * m], w1 = w[2 * m + 1];
-          const i32x4 a = {static_cast<int>(w0 & 0x0F0F0F0Fu), static_cast<int>((w0 >> 4) & 0x0F0F0F0Fu),
-                           static_cast<int>(w1 & 0x0F0F0F0Fu), static_cast<int>((w1 >> 4) & 0x0F0F0F0Fu)};
-          const i32x4 bx = *reinterpret_cast<const i32x4*>(xg + 16 * m);
-          d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx, d, 0, 0, 0);
-        }
-        const A8Meta mt = meta[mcol * G + g];
-        const float sx = col < B ? mt.s : 0.0f;
-        const int off = 8 * mt.sum;
-        const f4 f = {static_cast<float>(d[0] - off) * sx, static_cast<float>(d[1] - off) * sx,
-                      static_cast<float>(d[2] - off) * sx, static_cast<float>(d[3] - off) * sx};
-        scale_acc(acc, f, row_bcast2(swin, u));
-        if (i + kA8Depth < n_c) {  // refill the slot just consumed
-          const int gn = ksi + p.ks * (i + kA8Depth);
-          wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, lane * 16, gn * kBlockBytes, kStreamOnce);
-        }
-      }
+      block(u, i);
+      const int gn = ksi + p.ks * (i + kA8Depth);
+      wv[u] = __builtin_amdgcn_raw_buffer_load_b128(wrs, lane * 16, i + kA8Depth < n_c ? gn * kBlockBytes : wbytes,
+                                                    kStreamOnce);
     }
     swin = snext;
+  }
+  if (ib < n_c) {
+#pragma unroll
+    for (int u = 0; u < kA8Depth; ++u)
+      if (ib + u < n_c) block(u, ib + u);
   }
 
   // (5) K slices summed through LDS, then the epilogue on (tile, batch row, tile row) items

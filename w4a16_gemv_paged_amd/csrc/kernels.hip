@@ -35,7 +35,12 @@ namespace nq {
 // row are scaled by that row's fp16 group scale in fp32. Slices of a tile are
 // summed through LDS, then the fused epilogue runs on (tile, batch, row) items.
 
-constexpr int kDepth = 7;                   // 1 KiB weight loads in flight per wave
+// 1 KiB weight loads in flight per wave. With the ring kept full (below), 5
+// beat the earlier 7 on one box: batch-8 decode step 2.557 against 2.607 ms,
+// GEMV sweep aggregate 44.9% against 43.4% of 8 TB/s at batch 1 and 41.6%
+// against 39.9% at batch 4; 3, 4 and 6 came within 0.01 ms of 5 at batch 8,
+// 9 and 11 were slower (2.648, 2.688 ms).
+constexpr int kDepth = 5;
 constexpr int kGemvCUs = 256;               // MI355X compute units: one workgroup each in an even spread
 constexpr size_t kLdsMax = 160 * 1024;      // LDS of a workgroup on gfx950
 constexpr size_t kLdsX = 152 * 1024;        // LDS budget for staged activations and gain

@@ -60,6 +60,25 @@ def test_gemv_exact_arithmetic_bitwise(k, n, batch):
     np.testing.assert_array_equal(host(y).view(np.uint16), ref.view(np.uint16))
 
 
+@pytest.mark.parametrize("k", [640, 1280, 1408, 2560])
+@pytest.mark.parametrize("batch", [1, 4])
+def test_gemv_ring_windows_bitwise(k, batch):
+    """Wide matrices (1024 tiles: one K-slice per tile from batch 4, two at
+    batch 1) whose waves take 5, 10, 11 or 20 groups at batch 4 and 2-3, 5,
+    5-6 or 10 at batch 1: a lone last window of the weight ring, exactly one
+    or two full windows, full windows and a tail. Exact arithmetic as above,
+    so bit for bit."""
+    n = 16384
+    say("gemv ring windows", k, n, batch)
+    w, q, s = exact_case_weights(n, k, seed=k + 7)
+    rng = np.random.default_rng(batch + 10)
+    x = rng.integers(-2, 3, size=(batch, k)).astype(F16)
+    ref = oracle.gemv_w4a16(q, s, x).astype(F16)
+    y = torch.empty(batch, n, dtype=torch.float16, device="cuda")
+    nq.nq_gemv_w4a16(_packed_dev(w), n, k, 0, 0, batch, dev(x), None, 1e-6, None, y, nq.NQ_EPI_STORE_F16)
+    np.testing.assert_array_equal(host(y).view(np.uint16), ref.view(np.uint16))
+
+
 def test_gemv_one_hot_columns():
     """x = e_k returns column k: y[n] = fp16(q[n,k] * s[n, k // 128])."""
     k, n = 1024, 64
